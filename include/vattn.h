@@ -1,0 +1,112 @@
+/*
+ * vattn.h - head-major, non-causal attention over vision patches for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes.
+ *
+ * The operation (docs.rs page "rullama 0.1.0", source of
+ * src/kernels/wgsl/vision_attention_flash_sub_hpd_f16.wgsl: the Params
+ * uniform, the storage bindings and the head-major offsets of its Q stage,
+ * K/V tile loads and output store):
+ *
+ *   for every head h < n_heads and patch row i < n_patches
+ *     out[h][i][:] = sum_j softmax_j( sum_c q[h][i][c] * k[h][j][c] ) * v[h][j][:]
+ *
+ * where the softmax runs over every patch j < n_patches (non-causal: the
+ * shader visits every key tile for every query; no mask other than the
+ * patch count).  No scale is applied inside: the caller folds any 1/sqrt(d)
+ * into Q, as the shader's Params carries no scale field.
+ *
+ * Layout: q, k, v and out are float32, C-contiguous
+ * [n_heads][n_patches][head_dim]; element (h, i, c) sits at
+ * h*n_patches*head_dim + i*head_dim + c.
+ *
+ * Numerics: Q, K, V are rounded to f16 (round-to-nearest-even) for the matrix
+ * cores and all sums are accumulated in f32, with an online (running max /
+ * running sum) softmax.  The result is not bitwise equal to a float64
+ * evaluation; it is within max-abs 2e-3 and relative L2 1e-3 of it for inputs
+ * whose logits fit the precision mode (see vattn_precision).  Inputs must be
+ * finite with |q * log2(e)| and |k| below 65504 (the f16 range).
+ */
+#ifndef VATTN_H
+#define VATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum vattn_status {
+    VATTN_OK = 0,
+    VATTN_ERR_NULL = 1,      /* a tensor pointer is NULL while there is work  */
+    VATTN_ERR_SIZE = 2,      /* negative size, or a size the kernel's 32-bit
+                                per-head offsets / grid cannot address       */
+    VATTN_ERR_HEAD_DIM = 3,  /* head_dim is not 32 or 64                     */
+    VATTN_ERR_ALIGN = 4,     /* a tensor base address is not 16-byte aligned */
+    VATTN_ERR_ALIAS = 5,     /* out overlaps q, k or v                       */
+    VATTN_ERR_HIP = 6,       /* the HIP runtime refused the launch           */
+    VATTN_ERR_ARG = 7        /* unknown precision mode                       */
+} vattn_status;
+
+/* How the logits q.k are formed on the matrix cores.
+ *
+ * FAST:  one f16 x f16 product per logit (f32 accumulate).  The logit error
+ *        grows with |q| |k| (about 2^-11 relative per product), which is
+ *        fine while logits stay within a few tens.
+ * SPLIT: q = q_hi + q_lo and k = k_hi + k_lo with all four parts f16; the
+ *        logit is q_hi.k_hi + q_lo.k_hi + q_hi.k_lo (three f16 products, f32
+ *        accumulate), about 2^-21 relative per product.  Needed for sharp
+ *        softmax rows (logits of magnitude ~100 and above).  Twice the
+ *        matrix-core work of FAST for the Q.K^T half.
+ * AUTO:  the library chooses; currently SPLIT, the mode whose accuracy holds
+ *        for every input the f16 range admits.
+ */
+typedef enum vattn_precision {
+    VATTN_PRECISION_AUTO = 0,
+    VATTN_PRECISION_FAST = 1,
+    VATTN_PRECISION_SPLIT = 2
+} vattn_precision;
+
+/*
+ * vattn_forward - enqueue out = softmax(Q K^T) V for every head.
+ *
+ * q, k, v : device pointers, float32 [n_heads][n_patches][head_dim], read
+ *           only; they may alias one another.
+ * out     : device pointer, float32, same shape; every element is written.
+ *           It must not overlap q, k or v (VATTN_ERR_ALIAS).
+ * n_heads, n_patches : >= 0.  If either is 0 the call returns VATTN_OK and
+ *           enqueues nothing (pointers may then be NULL).
+ *           n_patches * head_dim must stay below 2^31.
+ * head_dim: 32 or 64.
+ * stream  : hipStream_t to enqueue on (NULL = the default stream).
+ *
+ * Ownership: the caller owns all four buffers and keeps them alive until the
+ * work on `stream` completes.  The library allocates nothing, keeps no state
+ * between calls and is safe to call from several threads.
+ *
+ * Errors: arguments are checked synchronously; on any error nothing is
+ * enqueued and `out` is untouched.  On VATTN_OK the kernel is enqueued and
+ * the call returns without synchronising; faults during execution surface at
+ * the caller's next synchronisation, as for any HIP kernel.
+ *
+ * Equivalent to vattn_forward_precision(..., VATTN_PRECISION_AUTO, stream).
+ */
+int vattn_forward(const float *q, const float *k, const float *v, float *out,
+                  int n_heads, int n_patches, int head_dim, void *stream);
+
+/* As vattn_forward, with an explicit vattn_precision mode (VATTN_ERR_ARG for
+ * an unknown one). */
+int vattn_forward_precision(const float *q, const float *k, const float *v,
+                            float *out, int n_heads, int n_patches,
+                            int head_dim, int precision, void *stream);
+
+/* Static, never-NULL description of a status code ("unknown status" for
+ * values outside vattn_status). */
+const char *vattn_status_string(int status);
+
+/* HIP error code (hipError_t) behind the last VATTN_ERR_HIP returned on the
+ * calling thread; 0 if none. */
+int vattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VATTN_H */

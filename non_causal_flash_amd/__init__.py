@@ -1,0 +1,129 @@
+"""Python binding of ``libvattn.so``: head-major, non-causal attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/vattn.h``.  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library is missing, importing this package raises.
+
+    import torch, non_causal_flash_amd as vattn
+    out = vattn.forward(q, k, v)            # q, k, v: cuda float32 [H, N, d]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch first: its bundled HIP runtime (soname libamdhip64.so.7) then serves
+# libvattn.so too, so the stream handles torch hands out are valid for it.
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvattn.so")
+
+VATTN_OK = 0
+VATTN_ERR_NULL = 1
+VATTN_ERR_SIZE = 2
+VATTN_ERR_HEAD_DIM = 3
+VATTN_ERR_ALIGN = 4
+VATTN_ERR_ALIAS = 5
+VATTN_ERR_HIP = 6
+VATTN_ERR_ARG = 7
+
+PRECISION = {"auto": 0, "fast": 1, "split": 2}
+
+# Symbols declared in include/vattn.h.
+EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_status_string",
+           "vattn_last_hip_error")
+
+
+class VattnError(RuntimeError):
+    def __init__(self, status: int, lib):
+        self.status = status
+        msg = lib.vattn_status_string(status).decode()
+        if status == VATTN_ERR_HIP:
+            msg += " (hipError_t %d)" % lib.vattn_last_hip_error()
+        super().__init__("vattn status %d: %s" % (status, msg))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libvattn.so is not built (%s); run `python -m non_causal_flash_amd.build`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.vattn_forward.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.vattn_forward.restype = ci
+    lib.vattn_forward_precision.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
+    lib.vattn_forward_precision.restype = ci
+    lib.vattn_status_string.argtypes = [ci]
+    lib.vattn_status_string.restype = ctypes.c_char_p
+    lib.vattn_last_hip_error.argtypes = []
+    lib.vattn_last_hip_error.restype = ci
+    return lib
+
+
+lib = _load()
+
+
+def forward_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
+                n_patches: int, head_dim: int, stream: int = 0,
+                precision: str | int = "auto") -> int:
+    """Direct call of ``vattn_forward_precision`` with raw device pointers.
+    Returns the status code (no exception)."""
+    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    return lib.vattn_forward_precision(q_ptr or None, k_ptr or None, v_ptr or None,
+                                       out_ptr or None, int(n_heads), int(n_patches),
+                                       int(head_dim), mode, stream or None)
+
+
+def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
+                  n_patches: int, head_dim: int, stream: int = 0) -> int:
+    """Direct call of the C entry point ``vattn_forward``; returns its status."""
+    return lib.vattn_forward(q_ptr or None, k_ptr or None, v_ptr or None,
+                             out_ptr or None, int(n_heads), int(n_patches),
+                             int(head_dim), stream or None)
+
+
+def _check(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device" % name)
+    if t.dim() != 3:
+        raise ValueError("%s must be [n_heads, n_patches, head_dim]" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            out: torch.Tensor | None = None, precision: str = "auto",
+            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """out[h] = softmax(q[h] @ k[h]^T) @ v[h] for every head (no scale inside).
+
+    q, k, v, out: float32, contiguous, [n_heads, n_patches, head_dim] on one
+    device, head_dim 32 or 64.  Enqueued on ``stream`` (default: torch's
+    current stream); returns ``out`` without synchronising.
+    """
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ: %s %s %s" % (q.shape, k.shape, v.shape))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out")
+    if out.shape != q.shape:
+        raise ValueError("out shape %s != %s" % (out.shape, q.shape))
+    devs = {q.device, k.device, v.device, out.device}
+    if len(devs) != 1:
+        raise ValueError("tensors on different devices: %s" % devs)
+    h, n, d = q.shape
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         h, n, d, s.cuda_stream, precision)
+    if rc != VATTN_OK:
+        raise VattnError(rc, lib)
+    return out

@@ -1,0 +1,44 @@
+"""Compile the gfx950 HIP library ``libvattn.so`` in-tree with hipcc.
+
+``python -m non_causal_flash_amd.build`` rebuilds it; ``build()`` is what the
+package's ``__graft_entry__.build()`` calls.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libvattn.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Build ``libvattn.so`` (always recompiles) and return its path."""
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, "vattn.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libvattn.so")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

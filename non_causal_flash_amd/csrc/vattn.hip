@@ -1,0 +1,98 @@
+// vattn.hip - C ABI of the MI355X head-major attention library: argument
+// checks, precision-mode choice and the kernel launch.  See include/vattn.h
+// for the contract of every entry point.
+#include "vattn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attention_fwd.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool overlaps(const void *a, const void *b, size_t bytes) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + bytes && pb < pa + bytes;
+}
+
+template <int D, bool SPLIT>
+hipError_t launch(const float *q, const float *k, const float *v, float *out,
+                  int n_patches, int q_blocks, int total_blocks,
+                  hipStream_t stream) {
+    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&out,
+                    (void *)&n_patches, (void *)&q_blocks, (void *)&total_blocks};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, SPLIT>),
+        dim3((unsigned)total_blocks), dim3(vattn::kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" const char *vattn_status_string(int status) {
+    switch (status) {
+        case VATTN_OK: return "ok";
+        case VATTN_ERR_NULL: return "null tensor pointer";
+        case VATTN_ERR_SIZE: return "invalid or too large size";
+        case VATTN_ERR_HEAD_DIM: return "head_dim must be 32 or 64";
+        case VATTN_ERR_ALIGN: return "tensor not 16-byte aligned";
+        case VATTN_ERR_ALIAS: return "out overlaps q, k or v";
+        case VATTN_ERR_HIP: return "HIP runtime error";
+        case VATTN_ERR_ARG: return "unknown precision mode";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int vattn_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int vattn_forward_precision(const float *q, const float *k,
+                                       const float *v, float *out, int n_heads,
+                                       int n_patches, int head_dim,
+                                       int precision, void *stream) {
+    if (n_heads < 0 || n_patches < 0) return VATTN_ERR_SIZE;
+    if (head_dim != 32 && head_dim != 64) return VATTN_ERR_HEAD_DIM;
+    if (precision != VATTN_PRECISION_AUTO && precision != VATTN_PRECISION_FAST &&
+        precision != VATTN_PRECISION_SPLIT)
+        return VATTN_ERR_ARG;
+    if (n_heads == 0 || n_patches == 0) return VATTN_OK;
+    if (!q || !k || !v || !out) return VATTN_ERR_NULL;
+
+    // Per-head offsets are 32-bit inside the kernel; the grid is 1-D.
+    const int64_t per_head = (int64_t)n_patches * head_dim;
+    const int64_t q_blocks = ((int64_t)n_patches + vattn::kBlockM - 1) / vattn::kBlockM;
+    const int64_t total_blocks = q_blocks * n_heads;
+    if (per_head >= ((int64_t)1 << 31) || total_blocks >= ((int64_t)1 << 31))
+        return VATTN_ERR_SIZE;
+
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
+    if (mis & 15u) return VATTN_ERR_ALIGN;
+
+    const size_t bytes = (size_t)per_head * (size_t)n_heads * sizeof(float);
+    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+        return VATTN_ERR_ALIAS;
+
+    const bool split = precision != VATTN_PRECISION_FAST;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (head_dim == 64)
+        err = split ? launch<64, true>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s)
+                    : launch<64, false>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s);
+    else
+        err = split ? launch<32, true>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s)
+                    : launch<32, false>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return VATTN_ERR_HIP;
+    }
+    return VATTN_OK;
+}
+
+extern "C" int vattn_forward(const float *q, const float *k, const float *v,
+                             float *out, int n_heads, int n_patches,
+                             int head_dim, void *stream) {
+    return vattn_forward_precision(q, k, v, out, n_heads, n_patches, head_dim,
+                                   VATTN_PRECISION_AUTO, stream);
+}

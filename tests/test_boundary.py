@@ -1,0 +1,108 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function ``include/vattn.h`` declares,
+and reject bad arguments synchronously with the documented status codes
+before any HIP call (the pointers passed here are never dereferenced).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vattn.h")
+
+import non_causal_flash_amd as vattn  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(vattn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(vattn.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_links_only_one_hip_runtime():
+    maps = open("/proc/self/maps").read()
+    hip = {m for m in re.findall(r"\S*libamdhip64\S*", maps)}
+    assert len(hip) == 1, hip
+
+
+def test_status_strings():
+    lib = vattn.lib
+    for code in range(8):
+        s = lib.vattn_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.vattn_status_string(99) == b"unknown status"
+    assert lib.vattn_status_string(-1) == b"unknown status"
+
+
+# Fake, 16-byte aligned, non-overlapping device addresses: validation fails
+# (or succeeds trivially) before anything would touch them.
+A, B, C, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, O, -1, 64, 64), vattn.VATTN_ERR_SIZE),
+    ((A, B, C, O, 4, -5, 64), vattn.VATTN_ERR_SIZE),
+    ((A, B, C, O, 4, 64, 48), vattn.VATTN_ERR_HEAD_DIM),
+    ((A, B, C, O, 4, 64, 128), vattn.VATTN_ERR_HEAD_DIM),
+    ((A, B, C, O, 4, 64, 0), vattn.VATTN_ERR_HEAD_DIM),
+    ((0, B, C, O, 4, 64, 64), vattn.VATTN_ERR_NULL),
+    ((A, 0, C, O, 4, 64, 64), vattn.VATTN_ERR_NULL),
+    ((A, B, 0, O, 4, 64, 64), vattn.VATTN_ERR_NULL),
+    ((A, B, C, 0, 4, 64, 64), vattn.VATTN_ERR_NULL),
+    ((A + 4, B, C, O, 4, 64, 64), vattn.VATTN_ERR_ALIGN),
+    ((A, B, C, O + 8, 4, 64, 64), vattn.VATTN_ERR_ALIGN),
+    ((A, B, C, A, 4, 64, 64), vattn.VATTN_ERR_ALIAS),
+    ((A, B, C, C + 4096, 4, 64, 64), vattn.VATTN_ERR_ALIAS),
+    ((A, B, C, B - 1024, 1, 64, 64), vattn.VATTN_ERR_ALIAS),
+    ((A, B, C, O, 1, 1 << 26, 64), vattn.VATTN_ERR_SIZE),
+    ((A, B, C, O, 1 << 30, 1 << 10, 32), vattn.VATTN_ERR_SIZE),
+    ((0, 0, 0, 0, 0, 64, 64), vattn.VATTN_OK),
+    ((0, 0, 0, 0, 4, 0, 64), vattn.VATTN_OK),
+])
+def test_argument_validation(args, status):
+    assert vattn.forward_raw(*args) == status
+    assert vattn.vattn_forward(*args) == status
+
+
+def test_unknown_precision_mode():
+    assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, 3) == vattn.VATTN_ERR_ARG
+    assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, -1) == vattn.VATTN_ERR_ARG
+
+
+def test_inputs_may_alias_each_other():
+    # q == k == v is allowed; only out must be disjoint.  Valid sizes reach
+    # the launch, so only check the no-device case on a machine without GPU.
+    if torch.cuda.is_available():
+        pytest.skip("launch would run on the GPU")
+    assert vattn.forward_raw(A, A, A, O, 1, 8, 32) == vattn.VATTN_ERR_HIP
+
+
+def test_no_device_reports_hip_error():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert vattn.forward_raw(A, B, C, O, 2, 100, 64) == vattn.VATTN_ERR_HIP
+    assert vattn.lib.vattn_last_hip_error() != 0
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    x = torch.zeros(2, 8, 64)
+    with pytest.raises(ValueError):
+        vattn.forward(x, x, x)  # CPU tensors
+    with pytest.raises(TypeError):
+        vattn.forward(x.double(), x, x)
