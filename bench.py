@@ -1,0 +1,170 @@
+"""Benchmark: head-major non-causal attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+
+One step is one ``vattn_forward`` over the whole workload (every head, every
+query row) on inputs already resident in HBM.  Prints one JSON line with the
+attention throughput 4*H*N^2*d / time, the roofline of the kernel against
+the dense f16 matrix-core peak, and the float64 CPU oracle timed on a bounded
+sample of the same workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (4·H·N²·d) + fraction of MFMA peak, 1 MI355X"
+PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16/bf16 matrix peak (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+KERNEL_SOURCES = ("non_causal_flash_amd/csrc/attention_fwd.hpp",
+                  "non_causal_flash_amd/csrc/vattn.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "attention_fwd_%s_traffic.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(q, k, v, w, target_s: float):
+    """The float64 oracle, untuned, on the first heads of the workload."""
+    import oracle
+    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
+    t0 = time.perf_counter()
+    oracle.attention_f64(q[:1], k[:1], v[:1], n_threads=cores)
+    t1 = time.perf_counter() - t0
+    heads = max(1, min(w.n_heads, int(round(target_s / max(t1, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.attention_f64(q[:heads], k[:heads], v[:heads], n_threads=cores)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * heads * w.n_patches ** 2 * w.head_dim
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "first %d of %d heads of %s, every row (%.1f s, float64, %d threads)"
+                      % (heads, w.n_heads, w.name, dt, cores)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 disables it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads are independent; see the sharding plan in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import non_causal_flash_amd as vattn
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    q, k, v = workloads.make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    out = torch.empty_like(dq)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        vattn.forward(dq, dk, dv, out=out, precision=args.precision)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        vattn.forward(dq, dk, dv, out=out, precision=args.precision)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    # spot parity on sampled rows (not timed)
+    import oracle
+    rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=2)
+    got = out.cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
+    ref = oracle.attention_rows_f64(q, k, v, rows)
+    diff = got - ref
+    parity = {"rows": int(rows.size), "max_abs": float(np.max(np.abs(diff))),
+              "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    traffic = read_traffic(w.name)
+    record = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_heads": w.n_heads, "n_patches": w.n_patches,
+                   "head_dim": w.head_dim, "precision": args.precision,
+                   "io": "f32 [H][N][d] resident in HBM"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                     "traffic": traffic},
+        "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
+        "parity_sample": parity,
+    }
+    if args.cpu_seconds > 0:
+        record["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_seconds)
+    else:
+        record["cpu_baseline"] = None
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,12 +109,13 @@ struct TileRegs {
     float4_t v[Shape<D>::kVKeys];
 };
 
-// Global -> registers.  Keys at or past `n_valid` read as zero (ragged tail).
-template <int D>
-__device__ __forceinline__ void load_tile(const float *__restrict__ kg,
-                                          const float *__restrict__ vg,
-                                          int key0, int n_valid,
-                                          TileRegs<D> &r, int tid) {
+// Global -> registers.  Keys at or past `n_valid` read as zero (ragged
+// tail); FULL tiles (n_valid == kTileN) skip the per-load guards.
+template <int D, bool FULL>
+__device__ __forceinline__ void load_tile_impl(const float *__restrict__ kg,
+                                               const float *__restrict__ vg,
+                                               int key0, int n_valid,
+                                               TileRegs<D> &r, int tid) {
     using S = Shape<D>;
     constexpr int kVecPerRow = D / 4;
 #pragma unroll
@@ -122,8 +123,8 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ kg,
         const int f = tid + kThreads * u;
         const int key = f / kVecPerRow;
         const int c = (f % kVecPerRow) * 4;
-        r.k[u] = key < n_valid ? load4(kg + (key0 + key) * D + c)
-                               : (float4_t){0.f, 0.f, 0.f, 0.f};
+        r.k[u] = (FULL || key < n_valid) ? load4(kg + (key0 + key) * D + c)
+                                         : (float4_t){0.f, 0.f, 0.f, 0.f};
     }
     // V: thread owns kVKeys consecutive keys x 4 consecutive dims.  Adjacent
     // lanes take adjacent key groups so the transposed LDS store below hits
@@ -133,9 +134,20 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ kg,
 #pragma unroll
     for (int e = 0; e < S::kVKeys; ++e) {
         const int key = kgi * S::kVKeys + e;
-        r.v[e] = key < n_valid ? load4(vg + (key0 + key) * D + 4 * c4)
-                               : (float4_t){0.f, 0.f, 0.f, 0.f};
+        r.v[e] = (FULL || key < n_valid) ? load4(vg + (key0 + key) * D + 4 * c4)
+                                         : (float4_t){0.f, 0.f, 0.f, 0.f};
     }
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(const float *__restrict__ kg,
+                                          const float *__restrict__ vg,
+                                          int key0, int n_valid,
+                                          TileRegs<D> &r, int tid) {
+    if (n_valid == kTileN)
+        load_tile_impl<D, true>(kg, vg, key0, n_valid, r, tid);
+    else
+        load_tile_impl<D, false>(kg, vg, key0, n_valid, r, tid);
 }
 
 // Registers -> LDS: K row-major [key][dim] (hi, and lo for SPLIT), V
