@@ -11,25 +11,28 @@
 // key-tile loop and online-softmax update).  This kernel keeps those ideas
 // and re-plans the rest for CDNA4:
 //
-//  * One workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//    rows.  Keys stream through LDS in tiles of 64, double buffered: while a
-//    tile is consumed, the next one is loaded from HBM/L2 into registers
-//    (coalesced float4 loads), converted to f16 with round-to-nearest-even
-//    and written to the other LDS buffer; one barrier per tile.
+//  * One workgroup = 8 waves = 128 query rows of one head; each wave owns 16
+//    rows, so a wave's state is small enough for 4 waves per SIMD: the
+//    vector ALUs only reach full issue rate with several waves, and the
+//    softmax is vector-ALU bound next to the matrix cores.
+//  * Keys stream through LDS in tiles of 64, double buffered.  Tile t+1 is
+//    loaded into registers with buffer loads (the hardware range check
+//    zero-fills rows past n_patches), converted to f16 with
+//    round-to-nearest-even and stored to the other LDS buffer while tile t
+//    is consumed; one barrier per tile.
 //  * Scores are produced transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_f16: the key fragment (A operand) comes from LDS,
-//    the query fragment (B operand) sits in registers for the whole kernel.
-//    In the 16x16 accumulator a lane then holds 4 keys of ONE query, so the
-//    row max / row sum are in-lane, plus two cross-lane steps per tile.
-//  * The probabilities P^T leave the accumulator as the B operand of the
-//    next product O^T = V^T P^T without any data movement: the key order the
-//    S accumulator hands out is matched by storing V^T in LDS with the same
-//    key permutation (see vt_pos).
-//  * log2(e) is folded into Q, so every exponential is one v_exp_f32
-//    (2^x).  The running max is only raised when a tile's max exceeds it by
-//    more than kRescaleSlack (then P <= 2^8, harmless in f16 and f32), so
-//    the O/l rescale is skipped for most tiles; the result is the same
-//    softmax, since any shift cancels between numerator and denominator.
+//    the query fragment (B operand) stays in registers.  In the 16x16
+//    accumulator a lane holds 4 keys of ONE query, so the row max / row sum
+//    are in-lane plus two cross-lane steps per tile.  The accumulator starts
+//    at -m (running max), so the matrix core also does the max subtraction.
+//  * The probabilities P^T leave the accumulator as the B operand of
+//    O^T = V^T P^T without data movement: V^T is stored in LDS with the same
+//    key permutation the S accumulator hands out (vt_pos).
+//  * log2(e) is folded into Q, so each exponential is one v_exp_f32 (2^x).
+//    The running max is only raised when a tile's max exceeds it by more than
+//    kRescaleSlack (P <= 2^8 is harmless in f16 and f32); the O/l rescale is
+//    a wave-uniform branch that is rare once the max settles.
 //  * The row sum l accumulates the f16-rounded P (v_dot2_f32_f16 against
 //    1.0), i.e. exactly the weights the P.V product uses.
 //  * SPLIT precision: q = q_hi + q_lo, k = k_hi + k_lo (all f16); the score
@@ -50,9 +53,9 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;            // 4 waves of 64
+constexpr int kThreads = 512;            // 8 waves of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowsPerWave = 32;         // two 16-row MFMA blocks
+constexpr int kRowsPerWave = 16;         // one 16-row MFMA block
 constexpr int kBlockM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kTileN = 64;               // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -61,14 +64,19 @@ constexpr float kRescaleSlack = 8.0f;    // log2 units
 template <int D>
 struct Shape {
     static_assert(D == 32 || D == 64, "head_dim must be 32 or 64");
-    static constexpr int kPad = 8;                   // halves; breaks LDS bank aliasing
+    // Row pad in halves.  ds_read_b128 of the MFMA fragments (lane l reads
+    // row l%16, column 16*(l/16) bytes) is free of bank conflicts on gfx950
+    // when the row pitch in 16-byte units is 2 mod 4 (measured: 96 and 160
+    // bytes are conflict-free, 80/112/144/176 bytes cost 4 extra cycles).
+    static constexpr int kPad = 16;
     static constexpr int kKRow = D + kPad;           // K row pitch in LDS (halves)
     static constexpr int kVRow = kTileN + kPad;      // V^T row pitch in LDS (halves)
     static constexpr int kKSteps = D / 32;           // 32-wide k-steps of Q.K^T
     static constexpr int kDBlocks = D / 16;          // 16-row blocks of O^T
     static constexpr int kKVec = kTileN * D / 4 / kThreads;  // K float4 per thread
-    static constexpr int kVKeys = D / 16;            // keys per thread in the V transpose
-    static constexpr int kVGroups = kTileN / kVKeys; // key groups per dim group
+    static constexpr int kVKeys = 2;                 // keys per thread in the V transpose
+    static constexpr int kVDims = kTileN * D / kThreads / kVKeys;  // dims per thread (4 or 2)
+    static constexpr int kVGroups = kTileN / kVKeys; // key pairs per dim group
 };
 
 // Storage position of key `key` (0..63) inside a V^T row.  Within each
@@ -102,99 +110,270 @@ __device__ __forceinline__ float4_t load4(const float *p) {
     return *reinterpret_cast<const float4_t *>(p);
 }
 
-// Registers holding one K/V tile between its global load and its LDS store.
+__device__ __forceinline__ float4_t zero4() { return (float4_t){0.f, 0.f, 0.f, 0.f}; }
+
+// Max / sum over the 4 lanes {l, l^16, l^32, l^48}, which hold one query's
+// keys.  v_permlane16_swap / v_permlane32_swap exchange 16-lane rows /
+// 32-lane halves between two registers; applied to two copies of x they put
+// the paired rows side by side.
+__device__ __forceinline__ float max_lane_groups(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+    const unsigned w = __builtin_bit_cast(unsigned, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
+// ---------------------------------------------------------------- tile I/O
+// Buffer descriptor over rows [key0, n_patches) of one head's K or V: loads
+// past the last row return 0 (hardware range check), so ragged tiles need no
+// guards and no address clamping in the vector ALUs.
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data, gfx9 descriptor layout
+
 template <int D>
-struct TileRegs {
-    float4_t k[Shape<D>::kKVec];
-    float4_t v[Shape<D>::kVKeys];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *head, int key0,
+                                                            int n_patches) {
+    const int rows = max(n_patches - key0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(head + (size_t)key0 * D),
+                                             (short)0, rows * D * (int)sizeof(float),
+                                             kBufferFlags);
+}
+
+__device__ __forceinline__ float4_t buf_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ float2_t buf_load2(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// Per-thread part of the tile layout (the same for every tile).
+//  K: float4 u of the thread is f = tid + kThreads*u of the tile: row
+//     f / (D/4), columns 4*(f % (D/4)) .. +3, so a wave reads whole rows.
+//  V: the thread owns kVKeys consecutive keys x kVDims consecutive dims, so
+//     the transposed LDS store writes both keys of one dim at once; adjacent
+//     lanes take adjacent key pairs, keeping those stores on distinct banks.
+template <int D>
+struct TileMap {
+    static constexpr int kRowStep = kThreads / (D / 4);  // K rows between u and u+1
+    int k_row0, k_col;   // K row of u = 0 and its column
+    int v_key0, v_dim0;  // first key and first dim of the thread's V block
+    __device__ __forceinline__ explicit TileMap(int tid) {
+        k_row0 = tid / (D / 4);
+        k_col = (tid % (D / 4)) * 4;
+        v_key0 = (tid % Shape<D>::kVGroups) * Shape<D>::kVKeys;
+        v_dim0 = (tid / Shape<D>::kVGroups) * Shape<D>::kVDims;
+    }
 };
 
-// Global -> registers.  Keys at or past `n_valid` read as zero (ragged
-// tail); FULL tiles (n_valid == kTileN) skip the per-load guards.
-template <int D, bool FULL>
-__device__ __forceinline__ void load_tile_impl(const float *__restrict__ kg,
-                                               const float *__restrict__ vg,
-                                               int key0, int n_valid,
-                                               TileRegs<D> &r, int tid) {
-    using S = Shape<D>;
-    constexpr int kVecPerRow = D / 4;
-#pragma unroll
-    for (int u = 0; u < S::kKVec; ++u) {
-        const int f = tid + kThreads * u;
-        const int key = f / kVecPerRow;
-        const int c = (f % kVecPerRow) * 4;
-        r.k[u] = (FULL || key < n_valid) ? load4(kg + (key0 + key) * D + c)
-                                         : (float4_t){0.f, 0.f, 0.f, 0.f};
-    }
-    // V: thread owns kVKeys consecutive keys x 4 consecutive dims.  Adjacent
-    // lanes take adjacent key groups so the transposed LDS store below hits
-    // distinct banks.
-    const int kgi = tid % S::kVGroups;
-    const int c4 = tid / S::kVGroups;
-#pragma unroll
-    for (int e = 0; e < S::kVKeys; ++e) {
-        const int key = kgi * S::kVKeys + e;
-        r.v[e] = (FULL || key < n_valid) ? load4(vg + (key0 + key) * D + 4 * c4)
-                                         : (float4_t){0.f, 0.f, 0.f, 0.f};
-    }
-}
+template <int N>
+struct FloatVec;
+template <>
+struct FloatVec<4> {
+    typedef float4_t type;
+};
+template <>
+struct FloatVec<2> {
+    typedef float2_t type;
+};
 
 template <int D>
-__device__ __forceinline__ void load_tile(const float *__restrict__ kg,
-                                          const float *__restrict__ vg,
-                                          int key0, int n_valid,
-                                          TileRegs<D> &r, int tid) {
-    if (n_valid == kTileN)
-        load_tile_impl<D, true>(kg, vg, key0, n_valid, r, tid);
-    else
-        load_tile_impl<D, false>(kg, vg, key0, n_valid, r, tid);
+struct TileRegs {
+    typedef typename FloatVec<Shape<D>::kVDims>::type VVec;
+    float4_t k[Shape<D>::kKVec];
+    VVec v[Shape<D>::kVKeys];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(const float *kg, const float *vg, int key0,
+                                          int n_patches, const TileMap<D> &m, TileRegs<D> &r) {
+    using S = Shape<D>;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kg, key0, n_patches);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vg, key0, n_patches);
+    const int koff = (m.k_row0 * D + m.k_col) * (int)sizeof(float);
+#pragma unroll
+    for (int u = 0; u < S::kKVec; ++u)
+        r.k[u] = buf_load4(rk, koff + u * TileMap<D>::kRowStep * D * (int)sizeof(float));
+    const int voff = (m.v_key0 * D + m.v_dim0) * (int)sizeof(float);
+#pragma unroll
+    for (int e = 0; e < S::kVKeys; ++e) {
+        if constexpr (S::kVDims == 4)
+            r.v[e] = buf_load4(rv, voff + e * D * (int)sizeof(float));
+        else
+            r.v[e] = buf_load2(rv, voff + e * D * (int)sizeof(float));
+    }
 }
 
-// Registers -> LDS: K row-major [key][dim] (hi, and lo for SPLIT), V
-// transposed [dim][vt_pos(key)].
+// Registers -> LDS: K row-major [key][dim] (and k_lo = f16(k - f32(f16(k)))
+// for SPLIT), V transposed [dim][vt_pos(key)].
 template <int D, bool SPLIT>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r,
-                                           _Float16 (*kh)[Shape<D>::kKRow],
+__device__ __forceinline__ void store_tile(const TileRegs<D> &r, _Float16 (*kh)[Shape<D>::kKRow],
                                            _Float16 (*kl)[Shape<D>::kKRow],
                                            _Float16 (*vt)[Shape<D>::kVRow],
-                                           int tid) {
+                                           const TileMap<D> &m) {
     using S = Shape<D>;
-    constexpr int kVecPerRow = D / 4;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int f = tid + kThreads * u;
-        const int key = f / kVecPerRow;
-        const int c = (f % kVecPerRow) * 4;
+        const int key = m.k_row0 + u * TileMap<D>::kRowStep;
         const half4_t hi = cvt4(r.k[u]);
-        *reinterpret_cast<half4_t *>(&kh[key][c]) = hi;
+        *reinterpret_cast<half4_t *>(&kh[key][m.k_col]) = hi;
         if constexpr (SPLIT) {
             const float4_t back = __builtin_convertvector(hi, float4_t);
-            *reinterpret_cast<half4_t *>(&kl[key][c]) = cvt4(r.k[u] - back);
+            *reinterpret_cast<half4_t *>(&kl[key][m.k_col]) = cvt4(r.k[u] - back);
         }
     }
-    const int kgi = tid % S::kVGroups;
-    const int c4 = tid / S::kVGroups;
-    const int pos = vt_pos(kgi * S::kVKeys);
+    const int pos = vt_pos(m.v_key0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if constexpr (S::kVKeys == 4) {
-            const half2_t a = cvt2(r.v[0][j], r.v[1][j]);
-            const half2_t b = cvt2(r.v[2][j], r.v[3][j]);
-            *reinterpret_cast<half4_t *>(&vt[4 * c4 + j][pos]) =
-                (half4_t){a[0], a[1], b[0], b[1]};
-        } else {
-            *reinterpret_cast<half2_t *>(&vt[4 * c4 + j][pos]) =
-                cvt2(r.v[0][j], r.v[1][j]);
-        }
-    }
+    for (int j = 0; j < S::kVDims; ++j)
+        *reinterpret_cast<half2_t *>(&vt[m.v_dim0 + j][pos]) = cvt2(r.v[0][j], r.v[1][j]);
 }
 
 __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// S'^T = K Q^T + C for one 64-key tile and the wave's 16 queries.  `c0`
+// starts every key block's accumulator at -m_ref, so the matrix core already
+// subtracts the running max from each logit.
 template <int D, bool SPLIT>
-__global__ void __launch_bounds__(kThreads)
+__device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Shape<D>::kKRow],
+                                        const _Float16 (*kl)[Shape<D>::kKRow],
+                                        const half8_t (&qh)[Shape<D>::kKSteps],
+                                        const half8_t (&ql)[Shape<D>::kKSteps], float4_t c0,
+                                        float4_t (&s)[4], int l16, int g4) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int st = 0; st < Shape<D>::kKSteps; ++st) {
+            const half8_t a = *reinterpret_cast<const half8_t *>(
+                &kh[16 * kb + l16][32 * st + 8 * g4]);
+            s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
+            if constexpr (SPLIT) {
+                s[kb] = mfma16(a, ql[st], s[kb]);
+                const half8_t al = *reinterpret_cast<const half8_t *>(
+                    &kl[16 * kb + l16][32 * st + 8 * g4]);
+                s[kb] = mfma16(al, qh[st], s[kb]);
+            }
+        }
+    }
+}
+
+// O^T += V^T P^T for one 64-key tile.
+template <int D>
+__device__ __forceinline__ void pv_tile(const _Float16 (*vt)[Shape<D>::kVRow],
+                                        const half8_t (&p)[2],
+                                        float4_t (&o)[Shape<D>::kDBlocks], int l16, int g4) {
+#pragma unroll
+    for (int db = 0; db < Shape<D>::kDBlocks; ++db) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const half8_t a = *reinterpret_cast<const half8_t *>(
+                &vt[16 * db + l16][32 * ks + 8 * g4]);
+            o[db] = mfma16(a, p[ks], o[db]);
+        }
+    }
+}
+
+__device__ __forceinline__ float max4(float4_t x) {
+    return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+}
+
+// P = 2^s as f16 MFMA operands (the key order of the S accumulator, matched
+// by vt_pos); l += the f16-rounded P.
+__device__ __forceinline__ void exp_tile(const float4_t (&s)[4], float &l_run, half8_t (&p)[2]) {
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float lsum = l_run;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        half2_t h[4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const float4_t x = s[2 * ks + hf];
+            h[2 * hf] = cvt2(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
+            h[2 * hf + 1] = cvt2(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lsum = __builtin_amdgcn_fdot2(h[j], ones, lsum, false);
+        p[ks] = (half8_t){h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    }
+    l_run = lsum;
+}
+
+// Online softmax and P.V for one tile whose scores s hold s_true - m_run
+// (the QK accumulator started at c0 = -m_run; before the first tile
+// m_run = -inf and c0 = 0).  The running max is raised only when the tile's
+// max exceeds it by more than kRescaleSlack: then o and l are scaled by
+// 2^(m_old - m_new), s is rebased and c0 follows.  That branch is
+// wave-uniform and rare once the max settles; it carries its own copy of
+// the exponentials and the P.V product, so the common path joins the rare
+// one only after values both sides compute afresh (no register copies).
+template <int D, bool MASK>
+__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, float &m_run,
+                                                float &l_run, float4_t (&o)[Shape<D>::kDBlocks],
+                                                const _Float16 (*vt)[Shape<D>::kVRow],
+                                                int key_lim, int l16, int g4) {
+    if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    mx = fmaxf(fmaxf(mx, s[0][3]), s[1][0]);
+    mx = fmaxf(fmaxf(mx, s[1][1]), s[1][2]);
+    mx = fmaxf(fmaxf(mx, s[1][3]), s[2][0]);
+    mx = fmaxf(fmaxf(mx, s[2][1]), s[2][2]);
+    mx = fmaxf(fmaxf(mx, s[2][3]), s[3][0]);
+    mx = fmaxf(fmaxf(mx, s[3][1]), s[3][2]);
+    mx = fmaxf(mx, s[3][3]);
+    const float m_ref = -c0[0];
+    const float tile_max = max_lane_groups(mx) + m_ref;
+    const bool raise = tile_max > m_run + kRescaleSlack;
+    half8_t p[2];
+    if (__ballot(raise)) {
+        const float m_new = raise ? tile_max : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float delta = m_new - m_ref;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < Shape<D>::kDBlocks; ++db) o[db] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[kb] -= delta;
+        c0 -= delta;
+        m_run = m_new;
+        exp_tile(s, l_run, p);
+        pv_tile<D>(vt, p, o, l16, g4);
+    } else {
+        exp_tile(s, l_run, p);
+        pv_tile<D>(vt, p, o, l16, g4);
+    }
+}
+
+template <int V>
+struct IntTag {
+    static constexpr int value = V;
+};
+
+// ------------------------------------------------------------------ kernel
+// Per key tile t (one barrier each): QK(t) from LDS buffer t%2, softmax,
+// PV(t); then tile t+1, already in registers, is converted into buffer
+// (t+1)%2 and the loads of tile t+2 are issued, so a tile's HBM/L2 latency
+// hides behind a whole tile of compute.  Matrix and vector work overlap
+// across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
+// buffer addresses are immediates.
+template <int D, bool SPLIT>
+__global__ void __launch_bounds__(kThreads, 4)
 attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
                      const float *__restrict__ v, float *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks) {
@@ -209,183 +388,81 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const int qblk = logical - head * q_blocks;
     const size_t base = (size_t)head * (size_t)n_patches * D;
     const float *__restrict__ qg = q + base;
-    const float *__restrict__ kg = k + base;
-    const float *__restrict__ vg = v + base;
+    const float *kg = k + base;
+    const float *vg = v + base;
     float *__restrict__ og = out + base;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int l16 = lane & 15;  // query column inside a 16-row block
+    const int l16 = lane & 15;  // query column inside the wave's 16 rows
     const int g4 = lane >> 4;   // lane group 0..3
-    const int row0 = qblk * kBlockM + wave * kRowsPerWave;
+    const int row = qblk * kBlockM + wave * kRowsPerWave + l16;
+    const int n_tiles = (n_patches + kTileN - 1) / kTileN;
+    const TileMap<D> map(tid);
 
-    // Query fragments (B operand of S^T = K Q^T), pre-multiplied by log2(e).
-    half8_t qh[2][S::kKSteps];
-    half8_t ql[2][S::kKSteps];
+    // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
+    half8_t qh[S::kKSteps];
+    half8_t ql[S::kKSteps];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int row = row0 + 16 * qb + l16;
-#pragma unroll
-        for (int st = 0; st < S::kKSteps; ++st) {
-            float4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-            if (row < n_patches) {
-                const float *p = qg + row * D + 32 * st + 8 * g4;
-                x0 = load4(p) * kLog2e;
-                x1 = load4(p + 4) * kLog2e;
-            }
-            const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
-            qh[qb][st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-            if constexpr (SPLIT) {
-                const half4_t e0 = cvt4(x0 - __builtin_convertvector(h0, float4_t));
-                const half4_t e1 = cvt4(x1 - __builtin_convertvector(h1, float4_t));
-                ql[qb][st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
-            }
+    for (int st = 0; st < S::kKSteps; ++st) {
+        float4_t x0 = zero4(), x1 = zero4();
+        if (row < n_patches) {
+            const float *p = qg + row * D + 32 * st + 8 * g4;
+            x0 = load4(p) * kLog2e;
+            x1 = load4(p + 4) * kLog2e;
+        }
+        const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
+        qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        if constexpr (SPLIT) {
+            const half4_t e0 = cvt4(x0 - __builtin_convertvector(h0, float4_t));
+            const half4_t e1 = cvt4(x1 - __builtin_convertvector(h1, float4_t));
+            ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+        } else {
+            ql[st] = qh[st];
         }
     }
 
-    float4_t o[2][S::kDBlocks];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int db = 0; db < S::kDBlocks; ++db) o[qb][db] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-    float l_run[2] = {0.f, 0.f};
-
-    const int n_tiles = (n_patches + kTileN - 1) / kTileN;
     TileRegs<D> regs;
-    load_tile<D>(kg, vg, 0, min(kTileN, n_patches), regs, tid);
-    store_tile<D, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], tid);
+    load_tile<D>(kg, vg, 0, n_patches, map, regs);
+    store_tile<D, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], map);
+    if (n_tiles > 1) load_tile<D>(kg, vg, kTileN, n_patches, map, regs);
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        const bool has_next = t + 1 < n_tiles;
-        if (has_next)
-            load_tile<D>(kg, vg, (t + 1) * kTileN,
-                         min(kTileN, n_patches - (t + 1) * kTileN), regs, tid);
+    float4_t o[S::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < S::kDBlocks; ++db) o[db] = zero4();
+    float m_run = -__builtin_inff();
+    float l_run = 0.f;
+    float4_t c0 = zero4();  // -(reference max) seeding every QK accumulator
 
-        // ---- S^T = K Q^T for 64 keys x 32 queries
-        float4_t s[2][4];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) s[qb][kb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-            for (int st = 0; st < S::kKSteps; ++st) {
-                const half8_t a = *reinterpret_cast<const half8_t *>(
-                    &kh_s[buf][16 * kb + l16][32 * st + 8 * g4]);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma16(a, qh[qb][st], s[qb][kb]);
-                if constexpr (SPLIT) {
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma16(a, ql[qb][st], s[qb][kb]);
-                    const half8_t al = *reinterpret_cast<const half8_t *>(
-                        &kl_s[buf][16 * kb + l16][32 * st + 8 * g4]);
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma16(al, qh[qb][st], s[qb][kb]);
-                }
-            }
-        }
-
-        // ---- keys past n_patches (only in the last tile)
+    auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        float4_t s[4];
+        qk_tile<D, SPLIT>(kh_s[BUF], kl_s[SPLIT ? BUF : 0], qh, ql, c0, s, l16, g4);
         const int key_lim = n_patches - t * kTileN;
-        if (key_lim < kTileN) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (16 * kb + 4 * g4 + i >= key_lim) {
-                        s[0][kb][i] = -__builtin_inff();
-                        s[1][kb][i] = -__builtin_inff();
-                    }
+        if (key_lim < kTileN)
+            softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+        else
+            softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+        if (t + 1 < n_tiles) {
+            store_tile<D, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0], vt_s[BUF ^ 1],
+                                 map);
+            if (t + 2 < n_tiles) load_tile<D>(kg, vg, (t + 2) * kTileN, n_patches, map, regs);
         }
-
-        // ---- online softmax: running max, rescale, P = 2^(s - m)
-        float m_new[2];
-        bool raise_any = false;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float mx = s[qb][0][0];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool raise = mx > m_run[qb] + kRescaleSlack;
-            m_new[qb] = raise ? mx : m_run[qb];
-            raise_any |= raise;
-        }
-        if (__any(raise_any)) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new[qb]);
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < S::kDBlocks; ++db) o[qb][db] *= alpha;
-                m_run[qb] = m_new[qb];
-            }
-        }
-
-        half8_t p[2][2];
-        const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float m = m_run[qb];
-            float lsum = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                half2_t h[4];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const float4_t x = s[qb][2 * ks + half];
-                    h[2 * half] = cvt2(__builtin_amdgcn_exp2f(x[0] - m),
-                                       __builtin_amdgcn_exp2f(x[1] - m));
-                    h[2 * half + 1] = cvt2(__builtin_amdgcn_exp2f(x[2] - m),
-                                           __builtin_amdgcn_exp2f(x[3] - m));
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) lsum = __builtin_amdgcn_fdot2(h[j], ones, lsum, false);
-                p[qb][ks] = (half8_t){h[0][0], h[0][1], h[1][0], h[1][1],
-                                      h[2][0], h[2][1], h[3][0], h[3][1]};
-            }
-            l_run[qb] += lsum;
-        }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int db = 0; db < S::kDBlocks; ++db) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const half8_t a = *reinterpret_cast<const half8_t *>(
-                    &vt_s[buf][16 * db + l16][32 * ks + 8 * g4]);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma16(a, p[qb][ks], o[qb][db]);
-            }
-        }
-
-        if (has_next)
-            store_tile<D, SPLIT>(regs, kh_s[buf ^ 1], kl_s[SPLIT ? (buf ^ 1) : 0],
-                                 vt_s[buf ^ 1], tid);
         __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, IntTag<0>{});
+        if (t + 1 < n_tiles) step(t + 1, IntTag<1>{});
     }
 
-    // ---- epilogue: out = O / l for rows inside the head
+    // Epilogue: out = O / l for rows inside the head.
+    const float inv = 1.0f / sum_lane_groups(l_run);
+    if (row < n_patches) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float lt = l_run[qb];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        const float inv = 1.0f / lt;
-        const int row = row0 + 16 * qb + l16;
-        if (row < n_patches) {
-#pragma unroll
-            for (int db = 0; db < S::kDBlocks; ++db)
-                *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[qb][db] * inv;
-        }
+        for (int db = 0; db < S::kDBlocks; ++db)
+            *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[db] * inv;
     }
 }
 
