@@ -74,7 +74,8 @@ typedef enum vattn_precision {
  *           It must not overlap q, k or v (VATTN_ERR_ALIAS).
  * n_heads, n_patches : >= 0.  If either is 0 the call returns VATTN_OK and
  *           enqueues nothing (pointers may then be NULL).
- *           n_patches * head_dim must stay below 2^31.
+ *           n_patches * head_dim must stay below 2^29 (one head's bytes
+ *           addressable with 32-bit offsets).
  * head_dim: 32 or 64.
  * stream  : hipStream_t to enqueue on (NULL = the default stream).
  *

@@ -11,10 +11,12 @@
 // key-tile loop and online-softmax update).  This kernel keeps those ideas
 // and re-plans the rest for CDNA4:
 //
-//  * One workgroup = 8 waves = 128 query rows of one head; each wave owns 16
-//    rows, so a wave's state is small enough for 4 waves per SIMD: the
-//    vector ALUs only reach full issue rate with several waves, and the
-//    softmax is vector-ALU bound next to the matrix cores.
+//  * One workgroup = WAVES waves (8 or 16) of one head; each wave owns 16
+//    query rows, so a wave's state is small enough for 4 waves per SIMD (the
+//    vector ALUs only reach full issue rate with several waves).  The whole
+//    workgroup shares each converted K/V tile, so 16 waves (256 rows) halve
+//    the K/V traffic from L2 and the conversion work per query; 8 waves
+//    (128 rows) give twice as many workgroups for small grids.
 //  * Keys stream through LDS in tiles of 64, double buffered.  Tile t+1 is
 //    loaded into registers with buffer loads (the hardware range check
 //    zero-fills rows past n_patches), converted to f16 with
@@ -53,30 +55,38 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;            // 8 waves of 64
-constexpr int kWaves = kThreads / 64;
-constexpr int kRowsPerWave = 16;         // one 16-row MFMA block
-constexpr int kBlockM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kRowsPerWave = 16;         // one 16-row MFMA block per wave
 constexpr int kTileN = 64;               // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 
+// LDS tile layout (the same for every workgroup size).
 template <int D>
-struct Shape {
+struct Lds {
     static_assert(D == 32 || D == 64, "head_dim must be 32 or 64");
     // Row pad in halves.  ds_read_b128 of the MFMA fragments (lane l reads
     // row l%16, column 16*(l/16) bytes) is free of bank conflicts on gfx950
     // when the row pitch in 16-byte units is 2 mod 4 (measured: 96 and 160
     // bytes are conflict-free, 80/112/144/176 bytes cost 4 extra cycles).
     static constexpr int kPad = 16;
-    static constexpr int kKRow = D + kPad;           // K row pitch in LDS (halves)
-    static constexpr int kVRow = kTileN + kPad;      // V^T row pitch in LDS (halves)
+    static constexpr int kKRow = D + kPad;           // K row pitch (halves)
+    static constexpr int kVRow = kTileN + kPad;      // V^T row pitch (halves)
     static constexpr int kKSteps = D / 32;           // 32-wide k-steps of Q.K^T
     static constexpr int kDBlocks = D / 16;          // 16-row blocks of O^T
-    static constexpr int kKVec = kTileN * D / 4 / kThreads;  // K float4 per thread
-    static constexpr int kVKeys = 2;                 // keys per thread in the V transpose
-    static constexpr int kVDims = kTileN * D / kThreads / kVKeys;  // dims per thread (4 or 2)
-    static constexpr int kVGroups = kTileN / kVKeys; // key pairs per dim group
+};
+
+// How the threads of a WAVES-wave workgroup share one K/V tile.
+template <int D, int WAVES>
+struct Shape {
+    static_assert(WAVES == 8 || WAVES == 16, "8 or 16 waves per workgroup");
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kBlockM = kRowsPerWave * WAVES;      // query rows per workgroup
+    static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) floats per thread
+    static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // floats per K load
+    static constexpr int kKVec = kTileElems / kKWidth;        // K loads per thread
+    static constexpr int kVKeys = 2;                          // keys per thread (V transpose)
+    static constexpr int kVDims = kTileElems / kVKeys;        // dims per thread: 4, 2 or 1
+    static constexpr int kVGroups = kTileN / kVKeys;          // key pairs per dim group
 };
 
 // Storage position of key `key` (0..63) inside a V^T row.  Within each
@@ -149,93 +159,117 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *head, i
                                              kBufferFlags);
 }
 
-__device__ __forceinline__ float4_t buf_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-__device__ __forceinline__ float2_t buf_load2(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
-}
-
-// Per-thread part of the tile layout (the same for every tile).
-//  K: float4 u of the thread is f = tid + kThreads*u of the tile: row
-//     f / (D/4), columns 4*(f % (D/4)) .. +3, so a wave reads whole rows.
-//  V: the thread owns kVKeys consecutive keys x kVDims consecutive dims, so
-//     the transposed LDS store writes both keys of one dim at once; adjacent
-//     lanes take adjacent key pairs, keeping those stores on distinct banks.
-template <int D>
-struct TileMap {
-    static constexpr int kRowStep = kThreads / (D / 4);  // K rows between u and u+1
-    int k_row0, k_col;   // K row of u = 0 and its column
-    int v_key0, v_dim0;  // first key and first dim of the thread's V block
-    __device__ __forceinline__ explicit TileMap(int tid) {
-        k_row0 = tid / (D / 4);
-        k_col = (tid % (D / 4)) * 4;
-        v_key0 = (tid % Shape<D>::kVGroups) * Shape<D>::kVKeys;
-        v_dim0 = (tid / Shape<D>::kVGroups) * Shape<D>::kVDims;
-    }
-};
-
 template <int N>
 struct FloatVec;
 template <>
 struct FloatVec<4> {
     typedef float4_t type;
+    typedef half4_t half_type;
 };
 template <>
 struct FloatVec<2> {
     typedef float2_t type;
+    typedef half2_t half_type;
+};
+template <>
+struct FloatVec<1> {
+    typedef float type;
+    typedef _Float16 half_type;
 };
 
-template <int D>
+template <int N>
+__device__ __forceinline__ typename FloatVec<N>::type buf_load(__amdgpu_buffer_rsrc_t r,
+                                                               int byte_off) {
+    if constexpr (N == 4)
+        return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    else if constexpr (N == 2)
+        return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    else
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+template <int N>
+__device__ __forceinline__ float elem(typename FloatVec<N>::type x, int j) {
+    if constexpr (N == 1)
+        return x;
+    else
+        return x[j];
+}
+
+// Per-thread part of the tile layout (the same for every tile).
+//  K: load u of the thread covers f = tid + kThreads*u of the tile in units
+//     of kKWidth floats: row f / (D/kKWidth), columns kKWidth*(f % ..), so a
+//     wave reads whole rows.
+//  V: the thread owns kVKeys consecutive keys x kVDims consecutive dims, so
+//     the transposed LDS store writes both keys of one dim at once; adjacent
+//     lanes take adjacent key pairs, keeping those stores on distinct banks.
+template <int D, int WAVES>
+struct TileMap {
+    using S = Shape<D, WAVES>;
+    static constexpr int kPerRow = D / S::kKWidth;           // K loads per row
+    static constexpr int kRowStep = S::kThreads / kPerRow;   // K rows between u and u+1
+    int k_row0, k_col;   // K row of u = 0 and its column
+    int v_key0, v_dim0;  // first key and first dim of the thread's V block
+    __device__ __forceinline__ explicit TileMap(int tid) {
+        k_row0 = tid / kPerRow;
+        k_col = (tid % kPerRow) * S::kKWidth;
+        v_key0 = (tid % S::kVGroups) * S::kVKeys;
+        v_dim0 = (tid / S::kVGroups) * S::kVDims;
+    }
+};
+
+template <int D, int WAVES>
 struct TileRegs {
-    typedef typename FloatVec<Shape<D>::kVDims>::type VVec;
-    float4_t k[Shape<D>::kKVec];
-    VVec v[Shape<D>::kVKeys];
+    using S = Shape<D, WAVES>;
+    typename FloatVec<S::kKWidth>::type k[S::kKVec];
+    typename FloatVec<S::kVDims>::type v[S::kVKeys];
 };
 
-template <int D>
+template <int D, int WAVES>
 __device__ __forceinline__ void load_tile(const float *kg, const float *vg, int key0,
-                                          int n_patches, const TileMap<D> &m, TileRegs<D> &r) {
-    using S = Shape<D>;
+                                          int n_patches, const TileMap<D, WAVES> &m,
+                                          TileRegs<D, WAVES> &r) {
+    using S = Shape<D, WAVES>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kg, key0, n_patches);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vg, key0, n_patches);
     const int koff = (m.k_row0 * D + m.k_col) * (int)sizeof(float);
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u)
-        r.k[u] = buf_load4(rk, koff + u * TileMap<D>::kRowStep * D * (int)sizeof(float));
+        r.k[u] = buf_load<S::kKWidth>(
+            rk, koff + u * TileMap<D, WAVES>::kRowStep * D * (int)sizeof(float));
     const int voff = (m.v_key0 * D + m.v_dim0) * (int)sizeof(float);
 #pragma unroll
-    for (int e = 0; e < S::kVKeys; ++e) {
-        if constexpr (S::kVDims == 4)
-            r.v[e] = buf_load4(rv, voff + e * D * (int)sizeof(float));
-        else
-            r.v[e] = buf_load2(rv, voff + e * D * (int)sizeof(float));
-    }
+    for (int e = 0; e < S::kVKeys; ++e)
+        r.v[e] = buf_load<S::kVDims>(rv, voff + e * D * (int)sizeof(float));
 }
 
 // Registers -> LDS: K row-major [key][dim] (and k_lo = f16(k - f32(f16(k)))
 // for SPLIT), V transposed [dim][vt_pos(key)].
-template <int D, bool SPLIT>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r, _Float16 (*kh)[Shape<D>::kKRow],
-                                           _Float16 (*kl)[Shape<D>::kKRow],
-                                           _Float16 (*vt)[Shape<D>::kVRow],
-                                           const TileMap<D> &m) {
-    using S = Shape<D>;
+template <int D, int WAVES, bool SPLIT>
+__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES> &r,
+                                           _Float16 (*kh)[Lds<D>::kKRow],
+                                           _Float16 (*kl)[Lds<D>::kKRow],
+                                           _Float16 (*vt)[Lds<D>::kVRow],
+                                           const TileMap<D, WAVES> &m) {
+    using S = Shape<D, WAVES>;
+    typedef typename FloatVec<S::kKWidth>::type KVec;
+    typedef typename FloatVec<S::kKWidth>::half_type KHalf;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int key = m.k_row0 + u * TileMap<D>::kRowStep;
-        const half4_t hi = cvt4(r.k[u]);
-        *reinterpret_cast<half4_t *>(&kh[key][m.k_col]) = hi;
+        const int key = m.k_row0 + u * TileMap<D, WAVES>::kRowStep;
+        const KHalf hi = __builtin_convertvector(r.k[u], KHalf);
+        *reinterpret_cast<KHalf *>(&kh[key][m.k_col]) = hi;
         if constexpr (SPLIT) {
-            const float4_t back = __builtin_convertvector(hi, float4_t);
-            *reinterpret_cast<half4_t *>(&kl[key][m.k_col]) = cvt4(r.k[u] - back);
+            const KVec back = __builtin_convertvector(hi, KVec);
+            *reinterpret_cast<KHalf *>(&kl[key][m.k_col]) =
+                __builtin_convertvector(r.k[u] - back, KHalf);
         }
     }
     const int pos = vt_pos(m.v_key0);
 #pragma unroll
     for (int j = 0; j < S::kVDims; ++j)
-        *reinterpret_cast<half2_t *>(&vt[m.v_dim0 + j][pos]) = cvt2(r.v[0][j], r.v[1][j]);
+        *reinterpret_cast<half2_t *>(&vt[m.v_dim0 + j][pos]) =
+            cvt2(elem<S::kVDims>(r.v[0], j), elem<S::kVDims>(r.v[1], j));
 }
 
 __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
@@ -246,15 +280,15 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // starts every key block's accumulator at -m_ref, so the matrix core already
 // subtracts the running max from each logit.
 template <int D, bool SPLIT>
-__device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Shape<D>::kKRow],
-                                        const _Float16 (*kl)[Shape<D>::kKRow],
-                                        const half8_t (&qh)[Shape<D>::kKSteps],
-                                        const half8_t (&ql)[Shape<D>::kKSteps], float4_t c0,
+__device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
+                                        const _Float16 (*kl)[Lds<D>::kKRow],
+                                        const half8_t (&qh)[Lds<D>::kKSteps],
+                                        const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
                                         float4_t (&s)[4], int l16, int g4) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int st = 0; st < Shape<D>::kKSteps; ++st) {
+        for (int st = 0; st < Lds<D>::kKSteps; ++st) {
             const half8_t a = *reinterpret_cast<const half8_t *>(
                 &kh[16 * kb + l16][32 * st + 8 * g4]);
             s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
@@ -270,11 +304,11 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Shape<D>::kKRow],
 
 // O^T += V^T P^T for one 64-key tile.
 template <int D>
-__device__ __forceinline__ void pv_tile(const _Float16 (*vt)[Shape<D>::kVRow],
+__device__ __forceinline__ void pv_tile(const _Float16 (*vt)[Lds<D>::kVRow],
                                         const half8_t (&p)[2],
-                                        float4_t (&o)[Shape<D>::kDBlocks], int l16, int g4) {
+                                        float4_t (&o)[Lds<D>::kDBlocks], int l16, int g4) {
 #pragma unroll
-    for (int db = 0; db < Shape<D>::kDBlocks; ++db) {
+    for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const half8_t a = *reinterpret_cast<const half8_t *>(
@@ -319,8 +353,8 @@ __device__ __forceinline__ void exp_tile(const float4_t (&s)[4], float &l_run, h
 // one only after values both sides compute afresh (no register copies).
 template <int D, bool MASK>
 __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, float &m_run,
-                                                float &l_run, float4_t (&o)[Shape<D>::kDBlocks],
-                                                const _Float16 (*vt)[Shape<D>::kVRow],
+                                                float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
+                                                const _Float16 (*vt)[Lds<D>::kVRow],
                                                 int key_lim, int l16, int g4) {
     if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
 #pragma unroll
@@ -347,7 +381,7 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, 
         const float delta = m_new - m_ref;
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < Shape<D>::kDBlocks; ++db) o[db] *= alpha;
+        for (int db = 0; db < Lds<D>::kDBlocks; ++db) o[db] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) s[kb] -= delta;
         c0 -= delta;
@@ -372,16 +406,17 @@ struct IntTag {
 // hides behind a whole tile of compute.  Matrix and vector work overlap
 // across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
-template <int D, bool SPLIT>
-__global__ void __launch_bounds__(kThreads, 4)
+template <int D, int WAVES, bool SPLIT>
+__global__ void __launch_bounds__(64 * WAVES, 4)
 attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
                      const float *__restrict__ v, float *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks) {
-    using S = Shape<D>;
-    __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][S::kKRow];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][D][S::kVRow];
+    using L = Lds<D>;
+    using S = Shape<D, WAVES>;
+    __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][D][L::kVRow];
     __shared__ __attribute__((aligned(16)))
-    _Float16 kl_s[SPLIT ? 2 : 1][SPLIT ? kTileN : 1][S::kKRow];
+    _Float16 kl_s[SPLIT ? 2 : 1][SPLIT ? kTileN : 1][L::kKRow];
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
@@ -397,15 +432,15 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const int lane = tid & 63;
     const int l16 = lane & 15;  // query column inside the wave's 16 rows
     const int g4 = lane >> 4;   // lane group 0..3
-    const int row = qblk * kBlockM + wave * kRowsPerWave + l16;
+    const int row = qblk * S::kBlockM + wave * kRowsPerWave + l16;
     const int n_tiles = (n_patches + kTileN - 1) / kTileN;
-    const TileMap<D> map(tid);
+    const TileMap<D, WAVES> map(tid);
 
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
-    half8_t qh[S::kKSteps];
-    half8_t ql[S::kKSteps];
+    half8_t qh[L::kKSteps];
+    half8_t ql[L::kKSteps];
 #pragma unroll
-    for (int st = 0; st < S::kKSteps; ++st) {
+    for (int st = 0; st < L::kKSteps; ++st) {
         float4_t x0 = zero4(), x1 = zero4();
         if (row < n_patches) {
             const float *p = qg + row * D + 32 * st + 8 * g4;
@@ -423,15 +458,15 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
         }
     }
 
-    TileRegs<D> regs;
-    load_tile<D>(kg, vg, 0, n_patches, map, regs);
-    store_tile<D, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], map);
-    if (n_tiles > 1) load_tile<D>(kg, vg, kTileN, n_patches, map, regs);
+    TileRegs<D, WAVES> regs;
+    load_tile<D, WAVES>(kg, vg, 0, n_patches, map, regs);
+    store_tile<D, WAVES, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], map);
+    if (n_tiles > 1) load_tile<D, WAVES>(kg, vg, kTileN, n_patches, map, regs);
     __syncthreads();
 
-    float4_t o[S::kDBlocks];
+    float4_t o[L::kDBlocks];
 #pragma unroll
-    for (int db = 0; db < S::kDBlocks; ++db) o[db] = zero4();
+    for (int db = 0; db < L::kDBlocks; ++db) o[db] = zero4();
     float m_run = -__builtin_inff();
     float l_run = 0.f;
     float4_t c0 = zero4();  // -(reference max) seeding every QK accumulator
@@ -446,9 +481,10 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
         else
             softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
         if (t + 1 < n_tiles) {
-            store_tile<D, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0], vt_s[BUF ^ 1],
-                                 map);
-            if (t + 2 < n_tiles) load_tile<D>(kg, vg, (t + 2) * kTileN, n_patches, map, regs);
+            store_tile<D, WAVES, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0],
+                                        vt_s[BUF ^ 1], map);
+            if (t + 2 < n_tiles)
+                load_tile<D, WAVES>(kg, vg, (t + 2) * kTileN, n_patches, map, regs);
         }
         __syncthreads();
     };
@@ -461,7 +497,7 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const float inv = 1.0f / sum_lane_groups(l_run);
     if (row < n_patches) {
 #pragma unroll
-        for (int db = 0; db < S::kDBlocks; ++db)
+        for (int db = 0; db < L::kDBlocks; ++db)
             *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[db] * inv;
     }
 }

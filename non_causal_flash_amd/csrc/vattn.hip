@@ -12,21 +12,39 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+constexpr int64_t kCusPerDevice = 256;  // MI355X compute units
+
 bool overlaps(const void *a, const void *b, size_t bytes) {
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
     const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
     return pa < pb + bytes && pb < pa + bytes;
 }
 
-template <int D, bool SPLIT>
+template <int D, int WAVES, bool SPLIT>
 hipError_t launch(const float *q, const float *k, const float *v, float *out,
-                  int n_patches, int q_blocks, int total_blocks,
-                  hipStream_t stream) {
+                  int n_heads, int n_patches, hipStream_t stream) {
+    constexpr int kBlockM = vattn::Shape<D, WAVES>::kBlockM;
+    int q_blocks = (n_patches + kBlockM - 1) / kBlockM;
+    int total_blocks = q_blocks * n_heads;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&out,
                     (void *)&n_patches, (void *)&q_blocks, (void *)&total_blocks};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, SPLIT>),
-        dim3((unsigned)total_blocks), dim3(vattn::kThreads), args, 0, stream);
+        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT>),
+        dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, stream);
+}
+
+// 16-wave workgroups (256 query rows) share each K/V tile among twice the
+// queries, halving L2 traffic and conversion work per query; they run one per
+// CU.  Use them when they still give every CU at least one workgroup.
+template <int D, bool SPLIT>
+hipError_t launch_any(const float *q, const float *k, const float *v, float *out,
+                      int n_heads, int n_patches, hipStream_t stream) {
+    const int64_t wide_blocks =
+        (int64_t)n_heads * (((int64_t)n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
+                            vattn::Shape<D, 16>::kBlockM);
+    if (wide_blocks >= kCusPerDevice)
+        return launch<D, 16, SPLIT>(q, k, v, out, n_heads, n_patches, stream);
+    return launch<D, 8, SPLIT>(q, k, v, out, n_heads, n_patches, stream);
 }
 
 }  // namespace
@@ -59,11 +77,12 @@ extern "C" int vattn_forward_precision(const float *q, const float *k,
     if (n_heads == 0 || n_patches == 0) return VATTN_OK;
     if (!q || !k || !v || !out) return VATTN_ERR_NULL;
 
-    // Per-head offsets are 32-bit inside the kernel; the grid is 1-D.
+    // Per-head byte offsets (and buffer-descriptor ranges) are 32-bit signed
+    // inside the kernel; the grid is 1-D (at most 128-row blocks).
     const int64_t per_head = (int64_t)n_patches * head_dim;
-    const int64_t q_blocks = ((int64_t)n_patches + vattn::kBlockM - 1) / vattn::kBlockM;
-    const int64_t total_blocks = q_blocks * n_heads;
-    if (per_head >= ((int64_t)1 << 31) || total_blocks >= ((int64_t)1 << 31))
+    const int64_t max_blocks = (int64_t)n_heads * (((int64_t)n_patches + 127) / 128);
+    if (per_head * (int64_t)sizeof(float) >= ((int64_t)1 << 31) ||
+        max_blocks >= ((int64_t)1 << 31))
         return VATTN_ERR_SIZE;
 
     const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
@@ -78,11 +97,11 @@ extern "C" int vattn_forward_precision(const float *q, const float *k,
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t err;
     if (head_dim == 64)
-        err = split ? launch<64, true>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s)
-                    : launch<64, false>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s);
+        err = split ? launch_any<64, true>(q, k, v, out, n_heads, n_patches, s)
+                    : launch_any<64, false>(q, k, v, out, n_heads, n_patches, s);
     else
-        err = split ? launch<32, true>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s)
-                    : launch<32, false>(q, k, v, out, n_patches, (int)q_blocks, (int)total_blocks, s);
+        err = split ? launch_any<32, true>(q, k, v, out, n_heads, n_patches, s)
+                    : launch_any<32, false>(q, k, v, out, n_heads, n_patches, s);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return VATTN_ERR_HIP;

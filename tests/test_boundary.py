@@ -71,6 +71,7 @@ A, B, C, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
     ((A, B, C, C + 4096, 4, 64, 64), vattn.VATTN_ERR_ALIAS),
     ((A, B, C, B - 1024, 1, 64, 64), vattn.VATTN_ERR_ALIAS),
     ((A, B, C, O, 1, 1 << 26, 64), vattn.VATTN_ERR_SIZE),
+    ((A, B, C, O, 1, 1 << 24, 32), vattn.VATTN_ERR_SIZE),
     ((A, B, C, O, 1 << 30, 1 << 10, 32), vattn.VATTN_ERR_SIZE),
     ((0, 0, 0, 0, 0, 64, 64), vattn.VATTN_OK),
     ((0, 0, 0, 0, 4, 0, 64), vattn.VATTN_OK),
