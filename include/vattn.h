@@ -53,11 +53,18 @@ typedef enum vattn_status {
  *        fine while logits stay within a few tens.
  * SPLIT: q = q_hi + q_lo and k = k_hi + k_lo with all four parts f16; the
  *        logit is q_hi.k_hi + q_lo.k_hi + q_hi.k_lo (three f16 products, f32
- *        accumulate), about 2^-21 relative per product.  Needed for sharp
- *        softmax rows (logits of magnitude ~100 and above).  Twice the
- *        matrix-core work of FAST for the Q.K^T half.
- * AUTO:  the library chooses; currently SPLIT, the mode whose accuracy holds
- *        for every input the f16 range admits.
+ *        accumulate), about 2^-21 relative per product, for every key.
+ *        Three times the matrix-core work of FAST for the Q.K^T half.
+ * AUTO:  SPLIT arithmetic where it can change the result, FAST elsewhere:
+ *        the two correction products are added to a block of 16 keys of a
+ *        16-query group only when some logit of the block lies within 16
+ *        (log2 units, i.e. weight 2^-16) of its query's running maximum, and
+ *        only for query groups whose running maximum exceeds 24 log2 units in
+ *        magnitude (where the f16 logit error ~2^-11 |logit| becomes
+ *        visible); the first key tile is always corrected.  Same accuracy as
+ *        SPLIT on sharp softmax rows at a fraction of its cost.  Inputs whose
+ *        logits are small only through cancellation of large |q| |k| should
+ *        use SPLIT.
  */
 typedef enum vattn_precision {
     VATTN_PRECISION_AUTO = 0,

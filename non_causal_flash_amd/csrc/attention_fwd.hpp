@@ -279,12 +279,19 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // S'^T = K Q^T + C for one 64-key tile and the wave's 16 queries.  `c0`
 // starts every key block's accumulator at -m_ref, so the matrix core already
 // subtracts the running max from each logit.
+//
+// SPLIT adds q_lo.k_hi + q_hi.k_lo to a 16-key block after the q_hi.k_hi
+// pass, but only where it can matter: when some lane's scores in the block
+// lie above -lo_window relative to m_ref (lo_window = +inf: every block,
+// -inf: none).  A key whose f16 logit sits more than lo_window below the
+// running max has weight below 2^-lo_window, so the ~2^-11 relative error
+// its q_hi.k_hi logit carries is negligible in the output.
 template <int D, bool SPLIT>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
                                         const half8_t (&qh)[Lds<D>::kKSteps],
                                         const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
-                                        float4_t (&s)[4], int l16, int g4) {
+                                        float4_t (&s)[4], int l16, int g4, float lo_window) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -292,11 +299,22 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
             const half8_t a = *reinterpret_cast<const half8_t *>(
                 &kh[16 * kb + l16][32 * st + 8 * g4]);
             s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
-            if constexpr (SPLIT) {
-                s[kb] = mfma16(a, ql[st], s[kb]);
-                const half8_t al = *reinterpret_cast<const half8_t *>(
-                    &kl[16 * kb + l16][32 * st + 8 * g4]);
-                s[kb] = mfma16(al, qh[st], s[kb]);
+        }
+    }
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float lane_max = fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3]));
+            if (__ballot(lane_max > -lo_window)) {
+#pragma unroll
+                for (int st = 0; st < Lds<D>::kKSteps; ++st) {
+                    const half8_t a = *reinterpret_cast<const half8_t *>(
+                        &kh[16 * kb + l16][32 * st + 8 * g4]);
+                    const half8_t al = *reinterpret_cast<const half8_t *>(
+                        &kl[16 * kb + l16][32 * st + 8 * g4]);
+                    s[kb] = mfma16(a, ql[st], s[kb]);
+                    s[kb] = mfma16(al, qh[st], s[kb]);
+                }
             }
         }
     }
@@ -400,9 +418,9 @@ struct IntTag {
 };
 
 // ------------------------------------------------------------------ kernel
-// Per key tile t (one barrier each): QK(t) from LDS buffer t%2, softmax,
-// PV(t); then tile t+1, already in registers, is converted into buffer
-// (t+1)%2 and the loads of tile t+2 are issued, so a tile's HBM/L2 latency
+// Per key tile t (one barrier each): tile t+1, already in registers, is
+// converted into LDS buffer (t+1)%2 and the loads of tile t+2 are issued;
+// then QK(t) from buffer t%2, softmax and PV(t).  A tile's HBM/L2 latency
 // hides behind a whole tile of compute.  Matrix and vector work overlap
 // across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
@@ -410,7 +428,8 @@ template <int D, int WAVES, bool SPLIT>
 __global__ void __launch_bounds__(64 * WAVES, 4)
 attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
                      const float *__restrict__ v, float *__restrict__ out,
-                     int n_patches, int q_blocks, int total_blocks) {
+                     int n_patches, int q_blocks, int total_blocks, float lo_window,
+                     float lo_gate) {
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
@@ -473,19 +492,31 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
 
     auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
         constexpr int BUF = decltype(buf_tag)::value;
-        float4_t s[4];
-        qk_tile<D, SPLIT>(kh_s[BUF], kl_s[SPLIT ? BUF : 0], qh, ql, c0, s, l16, g4);
-        const int key_lim = n_patches - t * kTileN;
-        if (key_lim < kTileN)
-            softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
-        else
-            softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+        // Tile t+1 (in registers since the previous step) into the LDS buffer
+        // tile t-1 used, then the loads of tile t+2: issued at the start, they
+        // drain while this tile is computed, and the stores have landed long
+        // before the barrier.
         if (t + 1 < n_tiles) {
             store_tile<D, WAVES, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0],
                                         vt_s[BUF ^ 1], map);
             if (t + 2 < n_tiles)
                 load_tile<D, WAVES>(kg, vg, (t + 2) * kTileN, n_patches, map, regs);
         }
+        float4_t s[4];
+        // Correction window of the SPLIT kernel: every block of the first
+        // tile (no running max yet); later, lo_window for waves whose running
+        // max has magnitude above lo_gate (large logits), none otherwise.
+        float win = __builtin_inff();
+        if constexpr (SPLIT) {
+            if (m_run != -__builtin_inff())
+                win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
+        }
+        qk_tile<D, SPLIT>(kh_s[BUF], kl_s[SPLIT ? BUF : 0], qh, ql, c0, s, l16, g4, win);
+        const int key_lim = n_patches - t * kTileN;
+        if (key_lim < kTileN)
+            softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+        else
+            softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
         __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {

@@ -14,20 +14,35 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kCusPerDevice = 256;  // MI355X compute units
 
+// AUTO precision: lo terms for key blocks within 16 log2 units (weight
+// > 2^-16) of the running max, in waves whose running max exceeds 24 log2
+// units in magnitude (f16 logit error ~2^-11 * |logit| > 0.01).
+constexpr float kAutoWindow = 16.0f;
+constexpr float kAutoGate = 24.0f;
+
 bool overlaps(const void *a, const void *b, size_t bytes) {
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
     const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
     return pa < pb + bytes && pb < pa + bytes;
 }
 
+// Correction policy of the SPLIT kernel (see qk_tile): the lo terms go to
+// key blocks within `window` (log2 units) of the running max, for waves
+// whose running max exceeds `gate` in magnitude.
+struct SplitPolicy {
+    float window;
+    float gate;
+};
+
 template <int D, int WAVES, bool SPLIT>
 hipError_t launch(const float *q, const float *k, const float *v, float *out,
-                  int n_heads, int n_patches, hipStream_t stream) {
+                  int n_heads, int n_patches, SplitPolicy pol, hipStream_t stream) {
     constexpr int kBlockM = vattn::Shape<D, WAVES>::kBlockM;
     int q_blocks = (n_patches + kBlockM - 1) / kBlockM;
     int total_blocks = q_blocks * n_heads;
-    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&out,
-                    (void *)&n_patches, (void *)&q_blocks, (void *)&total_blocks};
+    void *args[] = {(void *)&q,        (void *)&k,          (void *)&v,
+                    (void *)&out,      (void *)&n_patches,  (void *)&q_blocks,
+                    (void *)&total_blocks, (void *)&pol.window, (void *)&pol.gate};
     return hipLaunchKernel(
         reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT>),
         dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, stream);
@@ -38,13 +53,13 @@ hipError_t launch(const float *q, const float *k, const float *v, float *out,
 // CU.  Use them when they still give every CU at least one workgroup.
 template <int D, bool SPLIT>
 hipError_t launch_any(const float *q, const float *k, const float *v, float *out,
-                      int n_heads, int n_patches, hipStream_t stream) {
+                      int n_heads, int n_patches, SplitPolicy pol, hipStream_t stream) {
     const int64_t wide_blocks =
         (int64_t)n_heads * (((int64_t)n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
                             vattn::Shape<D, 16>::kBlockM);
     if (wide_blocks >= kCusPerDevice)
-        return launch<D, 16, SPLIT>(q, k, v, out, n_heads, n_patches, stream);
-    return launch<D, 8, SPLIT>(q, k, v, out, n_heads, n_patches, stream);
+        return launch<D, 16, SPLIT>(q, k, v, out, n_heads, n_patches, pol, stream);
+    return launch<D, 8, SPLIT>(q, k, v, out, n_heads, n_patches, pol, stream);
 }
 
 }  // namespace
@@ -94,14 +109,19 @@ extern "C" int vattn_forward_precision(const float *q, const float *k,
         return VATTN_ERR_ALIAS;
 
     const bool split = precision != VATTN_PRECISION_FAST;
+    const float inf = __builtin_inff();
+    // SPLIT: every key block, every wave.  AUTO: only near-max blocks of
+    // waves whose logits are large (kAutoWindow / kAutoGate).
+    const SplitPolicy pol = precision == VATTN_PRECISION_SPLIT ? SplitPolicy{inf, -1.0f}
+                                                               : SplitPolicy{kAutoWindow, kAutoGate};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t err;
     if (head_dim == 64)
-        err = split ? launch_any<64, true>(q, k, v, out, n_heads, n_patches, s)
-                    : launch_any<64, false>(q, k, v, out, n_heads, n_patches, s);
+        err = split ? launch_any<64, true>(q, k, v, out, n_heads, n_patches, pol, s)
+                    : launch_any<64, false>(q, k, v, out, n_heads, n_patches, pol, s);
     else
-        err = split ? launch_any<32, true>(q, k, v, out, n_heads, n_patches, s)
-                    : launch_any<32, false>(q, k, v, out, n_heads, n_patches, s);
+        err = split ? launch_any<32, true>(q, k, v, out, n_heads, n_patches, pol, s)
+                    : launch_any<32, false>(q, k, v, out, n_heads, n_patches, pol, s);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return VATTN_ERR_HIP;
