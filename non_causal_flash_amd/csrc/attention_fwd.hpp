@@ -29,8 +29,9 @@
 //    are in-lane plus two cross-lane steps per tile.  The accumulator starts
 //    at -m (running max), so the matrix core also does the max subtraction.
 //  * The probabilities P^T leave the accumulator as the B operand of
-//    O^T = V^T P^T without data movement: V^T is stored in LDS with the same
-//    key permutation the S accumulator hands out (vt_pos).
+//    O^T = V^T P^T without data movement.  V stays row-major in LDS, like K;
+//    the V^T operand is gathered with the gfx950 LDS transpose load
+//    (ds_read_b64_tr_b16) in the key order the S accumulator hands out.
 //  * log2(e) is folded into Q, so each exponential is one v_exp_f32 (2^x).
 //    The running max is only raised when a tile's max exceeds it by more than
 //    kRescaleSlack (P <= 2^8 is harmless in f16 and f32); the O/l rescale is
@@ -69,8 +70,7 @@ struct Lds {
     // when the row pitch in 16-byte units is 2 mod 4 (measured: 96 and 160
     // bytes are conflict-free, 80/112/144/176 bytes cost 4 extra cycles).
     static constexpr int kPad = 16;
-    static constexpr int kKRow = D + kPad;           // K row pitch (halves)
-    static constexpr int kVRow = kTileN + kPad;      // V^T row pitch (halves)
+    static constexpr int kKRow = D + kPad;           // K and V row pitch (halves)
     static constexpr int kKSteps = D / 32;           // 32-wide k-steps of Q.K^T
     static constexpr int kDBlocks = D / 16;          // 16-row blocks of O^T
 };
@@ -82,23 +82,9 @@ struct Shape {
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kBlockM = kRowsPerWave * WAVES;      // query rows per workgroup
     static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) floats per thread
-    static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // floats per K load
-    static constexpr int kKVec = kTileElems / kKWidth;        // K loads per thread
-    static constexpr int kVKeys = 2;                          // keys per thread (V transpose)
-    static constexpr int kVDims = kTileElems / kVKeys;        // dims per thread: 4, 2 or 1
-    static constexpr int kVGroups = kTileN / kVKeys;          // key pairs per dim group
+    static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // floats per load
+    static constexpr int kKVec = kTileElems / kKWidth;        // loads per thread per tensor
 };
-
-// Storage position of key `key` (0..63) inside a V^T row.  Within each
-// 32-key group the f16 P operand of lane group g (lanes 16g..16g+15) holds
-// keys {4g..4g+3} and {16+4g..16+4g+3}; the A operand of that lane group
-// reads positions 8g..8g+7, so position p must hold key
-// 16*bit2(p) + 8*bit4(p) + 4*bit3(p) + (p & 3).  Inverting: bits 4,3,2 of the
-// position are bits 3,2,4 of the key.
-__device__ __forceinline__ int vt_pos(int key) {
-    return (key & 0x23) | (((key >> 3) & 1) << 4) | (((key >> 2) & 1) << 3) |
-           (((key >> 4) & 1) << 2);
-}
 
 // Dispatch places workgroup b on XCD b % 8.  Give each XCD a contiguous run
 // of logical blocks (head-major), so one head's blocks share an L2.
@@ -196,25 +182,19 @@ __device__ __forceinline__ float elem(typename FloatVec<N>::type x, int j) {
         return x[j];
 }
 
-// Per-thread part of the tile layout (the same for every tile).
-//  K: load u of the thread covers f = tid + kThreads*u of the tile in units
-//     of kKWidth floats: row f / (D/kKWidth), columns kKWidth*(f % ..), so a
-//     wave reads whole rows.
-//  V: the thread owns kVKeys consecutive keys x kVDims consecutive dims, so
-//     the transposed LDS store writes both keys of one dim at once; adjacent
-//     lanes take adjacent key pairs, keeping those stores on distinct banks.
+// Per-thread part of the tile layout (the same for every tile): load u of
+// the thread covers f = tid + kThreads*u of the tile in units of kKWidth
+// floats, row f / (D/kKWidth), columns kKWidth*(f % ..), so a wave reads
+// whole rows.  K and V share the mapping.
 template <int D, int WAVES>
 struct TileMap {
     using S = Shape<D, WAVES>;
-    static constexpr int kPerRow = D / S::kKWidth;           // K loads per row
-    static constexpr int kRowStep = S::kThreads / kPerRow;   // K rows between u and u+1
-    int k_row0, k_col;   // K row of u = 0 and its column
-    int v_key0, v_dim0;  // first key and first dim of the thread's V block
+    static constexpr int kPerRow = D / S::kKWidth;           // loads per row
+    static constexpr int kRowStep = S::kThreads / kPerRow;   // rows between u and u+1
+    int row0, col;
     __device__ __forceinline__ explicit TileMap(int tid) {
-        k_row0 = tid / kPerRow;
-        k_col = (tid % kPerRow) * S::kKWidth;
-        v_key0 = (tid % S::kVGroups) * S::kVKeys;
-        v_dim0 = (tid / S::kVGroups) * S::kVDims;
+        row0 = tid / kPerRow;
+        col = (tid % kPerRow) * S::kKWidth;
     }
 };
 
@@ -222,7 +202,7 @@ template <int D, int WAVES>
 struct TileRegs {
     using S = Shape<D, WAVES>;
     typename FloatVec<S::kKWidth>::type k[S::kKVec];
-    typename FloatVec<S::kVDims>::type v[S::kVKeys];
+    typename FloatVec<S::kKWidth>::type v[S::kKVec];
 };
 
 template <int D, int WAVES>
@@ -232,44 +212,37 @@ __device__ __forceinline__ void load_tile(const float *kg, const float *vg, int 
     using S = Shape<D, WAVES>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kg, key0, n_patches);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vg, key0, n_patches);
-    const int koff = (m.k_row0 * D + m.k_col) * (int)sizeof(float);
+    const int off = (m.row0 * D + m.col) * (int)sizeof(float);
 #pragma unroll
-    for (int u = 0; u < S::kKVec; ++u)
-        r.k[u] = buf_load<S::kKWidth>(
-            rk, koff + u * TileMap<D, WAVES>::kRowStep * D * (int)sizeof(float));
-    const int voff = (m.v_key0 * D + m.v_dim0) * (int)sizeof(float);
-#pragma unroll
-    for (int e = 0; e < S::kVKeys; ++e)
-        r.v[e] = buf_load<S::kVDims>(rv, voff + e * D * (int)sizeof(float));
+    for (int u = 0; u < S::kKVec; ++u) {
+        const int o = off + u * TileMap<D, WAVES>::kRowStep * D * (int)sizeof(float);
+        r.k[u] = buf_load<S::kKWidth>(rk, o);
+        r.v[u] = buf_load<S::kKWidth>(rv, o);
+    }
 }
 
-// Registers -> LDS: K row-major [key][dim] (and k_lo = f16(k - f32(f16(k)))
-// for SPLIT), V transposed [dim][vt_pos(key)].
+// Registers -> LDS, both row-major [key][dim] in f16 (RNE); SPLIT also
+// stores k_lo = f16(k - f32(f16(k))).
 template <int D, int WAVES, bool SPLIT>
 __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
-                                           _Float16 (*vt)[Lds<D>::kVRow],
+                                           _Float16 (*vh)[Lds<D>::kKRow],
                                            const TileMap<D, WAVES> &m) {
     using S = Shape<D, WAVES>;
-    typedef typename FloatVec<S::kKWidth>::type KVec;
-    typedef typename FloatVec<S::kKWidth>::half_type KHalf;
+    typedef typename FloatVec<S::kKWidth>::type Vec;
+    typedef typename FloatVec<S::kKWidth>::half_type Half;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int key = m.k_row0 + u * TileMap<D, WAVES>::kRowStep;
-        const KHalf hi = __builtin_convertvector(r.k[u], KHalf);
-        *reinterpret_cast<KHalf *>(&kh[key][m.k_col]) = hi;
+        const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
+        const Half hi = __builtin_convertvector(r.k[u], Half);
+        *reinterpret_cast<Half *>(&kh[row][m.col]) = hi;
         if constexpr (SPLIT) {
-            const KVec back = __builtin_convertvector(hi, KVec);
-            *reinterpret_cast<KHalf *>(&kl[key][m.k_col]) =
-                __builtin_convertvector(r.k[u] - back, KHalf);
+            const Vec back = __builtin_convertvector(hi, Vec);
+            *reinterpret_cast<Half *>(&kl[row][m.col]) = __builtin_convertvector(r.k[u] - back, Half);
         }
+        *reinterpret_cast<Half *>(&vh[row][m.col]) = __builtin_convertvector(r.v[u], Half);
     }
-    const int pos = vt_pos(m.v_key0);
-#pragma unroll
-    for (int j = 0; j < S::kVDims; ++j)
-        *reinterpret_cast<half2_t *>(&vt[m.v_dim0 + j][pos]) =
-            cvt2(elem<S::kVDims>(r.v[0], j), elem<S::kVDims>(r.v[1], j));
 }
 
 __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
@@ -320,17 +293,34 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
     }
 }
 
-// O^T += V^T P^T for one 64-key tile.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+__device__ __forceinline__ half4_t read_tr16(const _Float16 *p) {
+    return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)p));
+}
+
+// O^T += V^T P^T for one 64-key tile.  The A operand (16 dims x 32 keys) is
+// two ds_read_b64_tr_b16 of row-major V: in each 16-lane group, lane s
+// points at 4 consecutive dims of one key row and output lane j receives
+// dim j of the 4 keys addressed by lanes j/4, j/4+4, j/4+8, j/4+12.  Lane s
+// of group g addresses key 4g + s/4 (+16 for the second read) at dims
+// 4*(s%4)..+3 of the block, which yields, for lane 16g+j, dim j of keys
+// {4g..4g+3} and {16+4g..16+4g+3}: the keys the P operand of that lane
+// holds, in the same order.
 template <int D>
-__device__ __forceinline__ void pv_tile(const _Float16 (*vt)[Lds<D>::kVRow],
+__device__ __forceinline__ void pv_tile(const _Float16 (*vh)[Lds<D>::kKRow],
                                         const half8_t (&p)[2],
                                         float4_t (&o)[Lds<D>::kDBlocks], int l16, int g4) {
+    const int key = 4 * g4 + (l16 >> 2);
+    const int dim = 4 * (l16 & 3);
 #pragma unroll
     for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const half8_t a = *reinterpret_cast<const half8_t *>(
-                &vt[16 * db + l16][32 * ks + 8 * g4]);
+            const half4_t a0 = read_tr16(&vh[32 * ks + key][16 * db + dim]);
+            const half4_t a1 = read_tr16(&vh[32 * ks + 16 + key][16 * db + dim]);
+            const half8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[db] = mfma16(a, p[ks], o[db]);
         }
     }
@@ -372,7 +362,7 @@ __device__ __forceinline__ void exp_tile(const float4_t (&s)[4], float &l_run, h
 template <int D, bool MASK>
 __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, float &m_run,
                                                 float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
-                                                const _Float16 (*vt)[Lds<D>::kVRow],
+                                                const _Float16 (*vt)[Lds<D>::kKRow],
                                                 int key_lim, int l16, int g4) {
     if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
 #pragma unroll
@@ -433,7 +423,7 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][D][L::kVRow];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
     _Float16 kl_s[SPLIT ? 2 : 1][SPLIT ? kTileN : 1][L::kKRow];
 
