@@ -48,7 +48,7 @@ class VattnError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            "libvattn.so is not built (%s); run `python -m non_causal_flash_amd.build`"
+            "libvattn.so is not built (%s); run `python non_causal_flash_amd/build.py`"
             % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, ci = ctypes.c_void_p, ctypes.c_int

@@ -1,6 +1,7 @@
 """Compile the gfx950 HIP library ``libvattn.so`` in-tree with hipcc.
 
-``python -m non_causal_flash_amd.build`` rebuilds it; ``build()`` is what the
+``python non_causal_flash_amd/build.py`` rebuilds it (run as a script: importing
+the package loads the library); ``build()`` is what the
 package's ``__graft_entry__.build()`` calls.
 """
 from __future__ import annotations
