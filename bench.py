@@ -100,8 +100,11 @@ def main():
     q, k, v = workloads.make_inputs(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    # Device tensors in the workload's storage order, seen as [H, N, d].
+    dq, dk, dv = (torch.from_numpy(workloads.to_layout(x, w.layout)).to(dev) for x in (q, k, v))
     out = torch.empty_like(dq)
+    if w.layout == "patch":
+        dq, dk, dv, out = (t.transpose(0, 1) for t in (dq, dk, dv, out))
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -128,7 +131,7 @@ def main():
     # spot parity on sampled rows (not timed)
     import oracle
     rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=2)
-    got = out.cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
+    got = out.contiguous().cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
     ref = oracle.attention_rows_f64(q, k, v, rows)
     diff = got - ref
     parity = {"rows": int(rows.size), "max_abs": float(np.max(np.abs(diff))),
@@ -151,7 +154,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_heads": w.n_heads, "n_patches": w.n_patches,
                    "head_dim": w.head_dim, "precision": args.precision,
-                   "io": "f32 [H][N][d] resident in HBM"},
+                   "io": "f32 %s resident in HBM" % ("[N][H][d]" if w.layout == "patch" else "[H][N][d]")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),

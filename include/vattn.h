@@ -15,9 +15,13 @@
  * patch count).  No scale is applied inside: the caller folds any 1/sqrt(d)
  * into Q, as the shader's Params carries no scale field.
  *
- * Layout: q, k, v and out are float32, C-contiguous
- * [n_heads][n_patches][head_dim]; element (h, i, c) sits at
- * h*n_patches*head_dim + i*head_dim + c.
+ * Layout: q, k, v and out are float32.  vattn_forward and
+ * vattn_forward_precision take the page's head-major layout, C-contiguous
+ * [n_heads][n_patches][head_dim]: element (h, i, c) sits at
+ * h*n_patches*head_dim + i*head_dim + c.  vattn_forward_strided takes any
+ * pair of row strides, e.g. the patch-major [n_patches][n_heads][head_dim]
+ * layout a fused QKV projection writes (the sibling of the page's
+ * head-major "HPD" buffers).
  *
  * Numerics: Q, K, V are rounded to f16 (round-to-nearest-even) for the matrix
  * cores and all sums are accumulated in f32, with an online (running max /
@@ -37,10 +41,13 @@ extern "C" {
 typedef enum vattn_status {
     VATTN_OK = 0,
     VATTN_ERR_NULL = 1,      /* a tensor pointer is NULL while there is work  */
-    VATTN_ERR_SIZE = 2,      /* negative size, or a size the kernel's 32-bit
-                                per-head offsets / grid cannot address       */
-    VATTN_ERR_HEAD_DIM = 3,  /* head_dim is not 32 or 64                     */
-    VATTN_ERR_ALIGN = 4,     /* a tensor base address is not 16-byte aligned */
+    VATTN_ERR_SIZE = 2,      /* negative size, strides that make rows overlap,
+                                or a size the kernel's 32-bit per-head offsets
+                                / grid cannot address                        */
+    VATTN_ERR_HEAD_DIM = 3,  /* head_dim is not in [1, 64]                   */
+    VATTN_ERR_ALIGN = 4,     /* a tensor base address is not aligned for its
+                                access mode (16 bytes, or 4 bytes when
+                                head_dim or a stride is not a multiple of 4)  */
     VATTN_ERR_ALIAS = 5,     /* out overlaps q, k or v                       */
     VATTN_ERR_HIP = 6,       /* the HIP runtime refused the launch           */
     VATTN_ERR_ARG = 7        /* unknown precision mode                       */
@@ -81,9 +88,11 @@ typedef enum vattn_precision {
  *           It must not overlap q, k or v (VATTN_ERR_ALIAS).
  * n_heads, n_patches : >= 0.  If either is 0 the call returns VATTN_OK and
  *           enqueues nothing (pointers may then be NULL).
- *           n_patches * head_dim must stay below 2^29 (one head's bytes
- *           addressable with 32-bit offsets).
- * head_dim: 32 or 64.
+ *           (n_patches + 63) * head_dim + head_dim must stay below 2^28 (one
+ *           head's bytes addressable with 32-bit offsets).
+ * head_dim: 1 ... 64.  32 and 64 run the contiguous fast path; other values
+ *           are zero-padded to 32 or 64 inside the kernel (the shader's own
+ *           limit is head_dim <= 64).
  * stream  : hipStream_t to enqueue on (NULL = the default stream).
  *
  * Ownership: the caller owns all four buffers and keeps them alive until the
@@ -105,6 +114,34 @@ int vattn_forward(const float *q, const float *k, const float *v, float *out,
 int vattn_forward_precision(const float *q, const float *k, const float *v,
                             float *out, int n_heads, int n_patches,
                             int head_dim, int precision, void *stream);
+
+/*
+ * vattn_forward_strided - as vattn_forward_precision, for tensors laid out
+ * with any pair of row strides.  Element (h, i, c) of q, k, v and out sits
+ * at h*stride_head + i*stride_patch + c (strides in floats, shared by the
+ * four tensors; the head_dim elements of a row are contiguous).
+ *
+ *   head-major  [n_heads][n_patches][head_dim]:
+ *       stride_head = n_patches*head_dim, stride_patch = head_dim
+ *   patch-major [n_patches][n_heads][head_dim]:
+ *       stride_head = head_dim,           stride_patch = n_heads*head_dim
+ *
+ * Rows must not overlap: stride_patch >= head_dim, stride_head >= head_dim,
+ * and either stride_head >= n_patches*stride_patch (heads outermost) or
+ * stride_patch >= n_heads*stride_head (patches outermost); otherwise
+ * VATTN_ERR_SIZE.  Also VATTN_ERR_SIZE when (n_patches + 63)*stride_patch +
+ * head_dim >= 2^28 or stride_patch >= 2^22.  Elements between rows (padding
+ * when a stride exceeds the row) are neither read nor written.  Base
+ * addresses must be 16-byte aligned, or 4-byte aligned when head_dim or a
+ * stride is not a multiple of 4 (that case loads single floats and is
+ * slower).  out must not overlap the address range of q, k or v.  Otherwise
+ * the contract of vattn_forward holds: synchronous checks, nothing enqueued
+ * on error, asynchronous on `stream` on success, no allocation.
+ */
+int vattn_forward_strided(const float *q, const float *k, const float *v,
+                          float *out, int n_heads, int n_patches, int head_dim,
+                          long long stride_head, long long stride_patch,
+                          int precision, void *stream);
 
 /* Static, never-NULL description of a status code ("unknown status" for
  * values outside vattn_status). */

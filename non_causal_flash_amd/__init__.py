@@ -7,6 +7,11 @@ library is missing, importing this package raises.
 
     import torch, non_causal_flash_amd as vattn
     out = vattn.forward(q, k, v)            # q, k, v: cuda float32 [H, N, d]
+
+``q``, ``k``, ``v`` (and ``out``) may also be strided views with the same
+strides and a contiguous last dimension, e.g. a patch-major ``[N, H, d]``
+tensor seen as ``x.transpose(0, 1)``; those go through
+``vattn_forward_strided``.
 """
 from __future__ import annotations
 
@@ -32,8 +37,8 @@ VATTN_ERR_ARG = 7
 PRECISION = {"auto": 0, "fast": 1, "split": 2}
 
 # Symbols declared in include/vattn.h.
-EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_status_string",
-           "vattn_last_hip_error")
+EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_forward_strided",
+           "vattn_status_string", "vattn_last_hip_error")
 
 
 class VattnError(RuntimeError):
@@ -56,6 +61,9 @@ def _load():
     lib.vattn_forward.restype = ci
     lib.vattn_forward_precision.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
     lib.vattn_forward_precision.restype = ci
+    ll = ctypes.c_longlong
+    lib.vattn_forward_strided.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp]
+    lib.vattn_forward_strided.restype = ci
     lib.vattn_status_string.argtypes = [ci]
     lib.vattn_status_string.restype = ctypes.c_char_p
     lib.vattn_last_hip_error.argtypes = []
@@ -77,6 +85,18 @@ def forward_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
                                        int(head_dim), mode, stream or None)
 
 
+def forward_strided_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
+                        n_patches: int, head_dim: int, stride_head: int, stride_patch: int,
+                        stream: int = 0, precision: str | int = "auto") -> int:
+    """Direct call of ``vattn_forward_strided`` (strides in floats); returns
+    the status code."""
+    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    return lib.vattn_forward_strided(q_ptr or None, k_ptr or None, v_ptr or None,
+                                     out_ptr or None, int(n_heads), int(n_patches),
+                                     int(head_dim), int(stride_head), int(stride_patch),
+                                     mode, stream or None)
+
+
 def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
                   n_patches: int, head_dim: int, stream: int = 0) -> int:
     """Direct call of the C entry point ``vattn_forward``; returns its status."""
@@ -94,8 +114,8 @@ def _check(t: torch.Tensor, name: str):
         raise ValueError("%s must be on a HIP device" % name)
     if t.dim() != 3:
         raise ValueError("%s must be [n_heads, n_patches, head_dim]" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("%s must have a contiguous last (head_dim) dimension" % name)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -103,8 +123,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """out[h] = softmax(q[h] @ k[h]^T) @ v[h] for every head (no scale inside).
 
-    q, k, v, out: float32, contiguous, [n_heads, n_patches, head_dim] on one
-    device, head_dim 32 or 64.  Enqueued on ``stream`` (default: torch's
+    q, k, v, out: float32 [n_heads, n_patches, head_dim] on one device,
+    head_dim <= 64, last dimension contiguous and the same strides for all
+    four (contiguous head-major tensors, or e.g. patch-major [N, H, d]
+    tensors viewed as ``x.transpose(0, 1)``).  ``out`` defaults to a new
+    tensor with q's strides.  Enqueued on ``stream`` (default: torch's
     current stream); returns ``out`` without synchronising.
     """
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -112,7 +135,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v shapes differ: %s %s %s" % (q.shape, k.shape, v.shape))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     _check(out, "out")
     if out.shape != q.shape:
         raise ValueError("out shape %s != %s" % (out.shape, q.shape))
@@ -120,10 +143,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if len(devs) != 1:
         raise ValueError("tensors on different devices: %s" % devs)
     h, n, d = q.shape
+    strides = {t.stride()[:2] for t in (q, k, v, out)}
+    if len(strides) != 1:
+        raise ValueError("q, k, v and out must share their strides: %s" % strides)
+    sh, sn = strides.pop()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream()
-        rc = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                         h, n, d, s.cuda_stream, precision)
+        if q.is_contiguous():
+            rc = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             h, n, d, s.cuda_stream, precision)
+        else:
+            rc = forward_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     h, n, d, sh, sn, s.cuda_stream, precision)
     if rc != VATTN_OK:
         raise VattnError(rc, lib)
     return out

@@ -43,6 +43,16 @@
 //  * Workgroup ids are remapped so that the query blocks of one head land
 //    on one XCD (dispatch is round-robin over the 8 XCDs), keeping that
 //    head's K/V in one L2.
+//  * Tensor access (IO): element (h, n, c) sits at h*stride_head +
+//    n*stride_patch + c.  kIoDense is the contiguous head-major layout with
+//    head_dim == D (the fast path: whole-row vector loads).  The strided
+//    modes cover any stride pair (e.g. the patch-major [n][h][c] layout a
+//    QKV projection writes) and any head_dim <= D: columns c >= head_dim are
+//    zero in every operand (their loads point past the buffer range, which
+//    the hardware returns as 0), so they add nothing to Q.K^T and the
+//    matching output columns are simply not stored.  kIoVec4 moves 4- (or
+//    2-) float vectors (head_dim and strides multiples of 4), kIoScalar
+//    single floats.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,6 +65,20 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kIoDense = 0;   // head-major, contiguous, head_dim == D
+constexpr int kIoVec4 = 1;    // strided, head_dim and strides multiples of 4
+constexpr int kIoScalar = 2;  // strided, any head_dim <= D
+
+// Strides (elements) and true head_dim of all four tensors.
+struct Io {
+    long long stride_head;
+    int stride_patch;
+    int head_dim;
+};
+
+// A byte offset past any buffer range: raw buffer loads there return 0.
+constexpr int kOutOfRange = 0x7ffffff0;
 
 constexpr int kRowsPerWave = 16;         // one 16-row MFMA block per wave
 constexpr int kTileN = 64;               // keys per LDS tile
@@ -136,13 +160,19 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // guards and no address clamping in the vector ALUs.
 constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data, gfx9 descriptor layout
 
-template <int D>
+template <int D, int IO>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *head, int key0,
-                                                            int n_patches) {
+                                                            int n_patches, const Io &io) {
     const int rows = max(n_patches - key0, 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(head + (size_t)key0 * D),
-                                             (short)0, rows * D * (int)sizeof(float),
-                                             kBufferFlags);
+    if constexpr (IO == kIoDense)
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(head + (size_t)key0 * D),
+                                                 (short)0, rows * D * (int)sizeof(float),
+                                                 kBufferFlags);
+    else
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(head + (size_t)key0 * io.stride_patch), (short)0,
+            rows > 0 ? ((rows - 1) * io.stride_patch + io.head_dim) * (int)sizeof(float) : 0,
+            kBufferFlags);
 }
 
 template <int N>
@@ -205,19 +235,41 @@ struct TileRegs {
     typename FloatVec<S::kKWidth>::type v[S::kKVec];
 };
 
-template <int D, int WAVES>
+// Vector of N floats at columns [col, col+N) of a row: the strided modes
+// move columns >= head_dim out of the buffer range (read as 0).
+template <int N, int IO>
+__device__ __forceinline__ typename FloatVec<N>::type load_cols(__amdgpu_buffer_rsrc_t r,
+                                                                int row_off, int col,
+                                                                const Io &io) {
+    if constexpr (IO == kIoScalar) {
+        typename FloatVec<N>::type x;
+        if constexpr (N == 1) {
+            x = buf_load<1>(r, col < io.head_dim ? (row_off + col) * 4 : kOutOfRange);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                x[j] = buf_load<1>(r, col + j < io.head_dim ? (row_off + col + j) * 4 : kOutOfRange);
+        }
+        return x;
+    } else {
+        const bool in = IO == kIoDense || col < io.head_dim;
+        return buf_load<N>(r, in ? (row_off + col) * 4 : kOutOfRange);
+    }
+}
+
+template <int D, int WAVES, int IO>
 __device__ __forceinline__ void load_tile(const float *kg, const float *vg, int key0,
                                           int n_patches, const TileMap<D, WAVES> &m,
-                                          TileRegs<D, WAVES> &r) {
+                                          TileRegs<D, WAVES> &r, const Io &io) {
     using S = Shape<D, WAVES>;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kg, key0, n_patches);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vg, key0, n_patches);
-    const int off = (m.row0 * D + m.col) * (int)sizeof(float);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
+    const int pitch = IO == kIoDense ? D : io.stride_patch;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int o = off + u * TileMap<D, WAVES>::kRowStep * D * (int)sizeof(float);
-        r.k[u] = buf_load<S::kKWidth>(rk, o);
-        r.v[u] = buf_load<S::kKWidth>(rv, o);
+        const int row_off = (m.row0 + u * TileMap<D, WAVES>::kRowStep) * pitch;
+        r.k[u] = load_cols<S::kKWidth, IO>(rk, row_off, m.col, io);
+        r.v[u] = load_cols<S::kKWidth, IO>(rv, row_off, m.col, io);
     }
 }
 
@@ -414,12 +466,12 @@ struct IntTag {
 // hides behind a whole tile of compute.  Matrix and vector work overlap
 // across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
-template <int D, int WAVES, bool SPLIT>
+template <int D, int WAVES, bool SPLIT, int IO>
 __global__ void __launch_bounds__(64 * WAVES, 4)
 attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
                      const float *__restrict__ v, float *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks, float lo_window,
-                     float lo_gate) {
+                     float lo_gate, Io io) {
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
@@ -430,7 +482,8 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
     const int qblk = logical - head * q_blocks;
-    const size_t base = (size_t)head * (size_t)n_patches * D;
+    const size_t base = IO == kIoDense ? (size_t)head * (size_t)n_patches * D
+                                       : (size_t)((long long)head * io.stride_head);
     const float *__restrict__ qg = q + base;
     const float *kg = k + base;
     const float *vg = v + base;
@@ -448,14 +501,24 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
+    __amdgpu_buffer_rsrc_t rq;
+    if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
 #pragma unroll
     for (int st = 0; st < L::kKSteps; ++st) {
         float4_t x0 = zero4(), x1 = zero4();
-        if (row < n_patches) {
-            const float *p = qg + row * D + 32 * st + 8 * g4;
-            x0 = load4(p) * kLog2e;
-            x1 = load4(p + 4) * kLog2e;
+        const int c = 32 * st + 8 * g4;
+        if constexpr (IO == kIoDense) {
+            if (row < n_patches) {
+                const float *p = qg + row * D + c;
+                x0 = load4(p);
+                x1 = load4(p + 4);
+            }
+        } else if (row < n_patches) {
+            x0 = load_cols<4, IO>(rq, row * io.stride_patch, c, io);
+            x1 = load_cols<4, IO>(rq, row * io.stride_patch, c + 4, io);
         }
+        x0 *= kLog2e;
+        x1 *= kLog2e;
         const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
         qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
         if constexpr (SPLIT) {
@@ -468,9 +531,9 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     }
 
     TileRegs<D, WAVES> regs;
-    load_tile<D, WAVES>(kg, vg, 0, n_patches, map, regs);
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
     store_tile<D, WAVES, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], map);
-    if (n_tiles > 1) load_tile<D, WAVES>(kg, vg, kTileN, n_patches, map, regs);
+    if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
     __syncthreads();
 
     float4_t o[L::kDBlocks];
@@ -490,7 +553,7 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
             store_tile<D, WAVES, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0],
                                         vt_s[BUF ^ 1], map);
             if (t + 2 < n_tiles)
-                load_tile<D, WAVES>(kg, vg, (t + 2) * kTileN, n_patches, map, regs);
+                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
         }
         float4_t s[4];
         // Correction window of the SPLIT kernel: every block of the first
@@ -514,12 +577,29 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
         if (t + 1 < n_tiles) step(t + 1, IntTag<1>{});
     }
 
-    // Epilogue: out = O / l for rows inside the head.
+    // Epilogue: out = O / l for rows inside the head (and, in the strided
+    // modes, columns below head_dim).
     const float inv = 1.0f / sum_lane_groups(l_run);
     if (row < n_patches) {
+        if constexpr (IO == kIoDense) {
 #pragma unroll
-        for (int db = 0; db < L::kDBlocks; ++db)
-            *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[db] * inv;
+            for (int db = 0; db < L::kDBlocks; ++db)
+                *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[db] * inv;
+        } else {
+            float *orow = og + (size_t)row * io.stride_patch;
+#pragma unroll
+            for (int db = 0; db < L::kDBlocks; ++db) {
+                const int c = 16 * db + 4 * g4;
+                const float4_t y = o[db] * inv;
+                if constexpr (IO == kIoVec4) {
+                    if (c < io.head_dim) *reinterpret_cast<float4_t *>(orow + c) = y;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (c + j < io.head_dim) orow[c + j] = y[j];
+                }
+            }
+        }
     }
 }
 

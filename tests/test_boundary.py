@@ -58,7 +58,7 @@ A, B, C, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 @pytest.mark.parametrize("args,status", [
     ((A, B, C, O, -1, 64, 64), vattn.VATTN_ERR_SIZE),
     ((A, B, C, O, 4, -5, 64), vattn.VATTN_ERR_SIZE),
-    ((A, B, C, O, 4, 64, 48), vattn.VATTN_ERR_HEAD_DIM),
+    ((A, B, C, O, 4, 64, 65), vattn.VATTN_ERR_HEAD_DIM),
     ((A, B, C, O, 4, 64, 128), vattn.VATTN_ERR_HEAD_DIM),
     ((A, B, C, O, 4, 64, 0), vattn.VATTN_ERR_HEAD_DIM),
     ((0, B, C, O, 4, 64, 64), vattn.VATTN_ERR_NULL),
@@ -72,6 +72,8 @@ A, B, C, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
     ((A, B, C, B - 1024, 1, 64, 64), vattn.VATTN_ERR_ALIAS),
     ((A, B, C, O, 1, 1 << 26, 64), vattn.VATTN_ERR_SIZE),
     ((A, B, C, O, 1, 1 << 24, 32), vattn.VATTN_ERR_SIZE),
+    ((A, B, C, O, 1, (1 << 22) - 63, 64), vattn.VATTN_ERR_SIZE),
+    ((A + 4, B, C, O, 4, 64, 40), vattn.VATTN_ERR_ALIGN),
     ((A, B, C, O, 1 << 30, 1 << 10, 32), vattn.VATTN_ERR_SIZE),
     ((0, 0, 0, 0, 0, 64, 64), vattn.VATTN_OK),
     ((0, 0, 0, 0, 4, 0, 64), vattn.VATTN_OK),
@@ -79,6 +81,50 @@ A, B, C, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
 def test_argument_validation(args, status):
     assert vattn.forward_raw(*args) == status
     assert vattn.vattn_forward(*args) == status
+
+
+H, N = 4, 100
+# (args after the pointers: n_heads, n_patches, head_dim, stride_head, stride_patch)
+STRIDED_CASES = [
+    ((H, N, 64, 64, 64), vattn.VATTN_ERR_SIZE),            # heads overlap patches
+    ((H, N, 64, N * 64, 32), vattn.VATTN_ERR_SIZE),        # stride_patch < head_dim
+    ((H, N, 64, 32, H * 64), vattn.VATTN_ERR_SIZE),        # stride_head < head_dim
+    ((H, N, 64, 64, H * 64 - 4), vattn.VATTN_ERR_SIZE),    # patch rows overlap
+    ((H, N, 40, N * 48 - 4, 48), vattn.VATTN_ERR_SIZE),    # heads overlap
+    ((H, 1 << 20, 64, 64, H * 64), vattn.VATTN_ERR_SIZE),  # span past 2^28
+    ((H, N, 0, N * 64, 64), vattn.VATTN_ERR_HEAD_DIM),
+    ((H, N, 65, N * 65, 65), vattn.VATTN_ERR_HEAD_DIM),
+    ((0, N, 64, 64, 0), vattn.VATTN_OK),                   # nothing to do
+]
+
+
+@pytest.mark.parametrize("args,status", STRIDED_CASES)
+def test_strided_argument_validation(args, status):
+    assert vattn.forward_strided_raw(A, B, C, O, *args) == status
+
+
+@pytest.mark.parametrize("args,offset,status", [
+    # 16-byte alignment needed unless head_dim or a stride is not a multiple of 4
+    ((H, N, 64, 64, H * 64), 4, vattn.VATTN_ERR_ALIGN),
+    ((H, N, 40, N * 48, 48), 8, vattn.VATTN_ERR_ALIGN),
+    ((H, N, 41, N * 41, 41), 2, vattn.VATTN_ERR_ALIGN),
+])
+def test_strided_alignment(args, offset, status):
+    assert vattn.forward_strided_raw(A + offset, B, C, O, *args) == status
+
+
+def test_strided_alias_uses_the_strided_extent():
+    # patch-major: the tensor spans N * H * d floats; out starting inside it aliases
+    span = N * H * 64 * 4
+    assert vattn.forward_strided_raw(A, B, C, A + span - 256, H, N, 64, 64, H * 64) == \
+        vattn.VATTN_ERR_ALIAS
+
+
+def test_scalar_mode_accepts_4_byte_alignment():
+    if torch.cuda.is_available():
+        pytest.skip("launch would run on the GPU")
+    # head_dim 41: single-float accesses, so a 4-byte aligned base reaches the launch
+    assert vattn.forward_strided_raw(A + 4, B, C, O, H, N, 41, N * 41, 41) == vattn.VATTN_ERR_HIP
 
 
 def test_unknown_precision_mode():
@@ -107,3 +153,5 @@ def test_python_wrapper_rejects_bad_tensors():
         vattn.forward(x, x, x)  # CPU tensors
     with pytest.raises(TypeError):
         vattn.forward(x.double(), x, x)
+    with pytest.raises(ValueError):
+        vattn.forward(x, x, x.transpose(1, 2).contiguous().transpose(1, 2))  # strided last dim

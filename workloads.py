@@ -21,7 +21,14 @@ id    H       N       d         distribution
 4     12      4097    32        Q ~ N(0,1)/sqrt(32), K, V ~ N(0,1) (ragged tails)
 5     128     4096    64        Q, K ~ N(0, 3^2) unscaled, V ~ U(-1,1)
                                 (16 heads x 8 images; sharp softmax)
+6     128     4096    64        as 5, stored patch-major [N][H][d]
+7     16      1024    40        Q ~ N(0,1)/sqrt(40), K, V ~ N(0,1) (head_dim 40)
 ====  ======  ======  ========  ===================================================
+
+Workloads 1-5 are the head-major [H][N][d] cases; 6 and 7 exercise the
+strided (patch-major) access and a head_dim that is neither 32 nor 64.
+``make_inputs`` always returns head-major arrays; ``to_layout`` gives the
+storage order a workload is run in.
 
 The default seed of workload ``i`` is ``1000 + i``.
 """
@@ -40,6 +47,7 @@ class Workload:
     n_patches: int
     head_dim: int
     kind: str  # "normal" or "sharp"
+    layout: str = "head"  # "head": [H][N][d]; "patch": [N][H][d]
 
     @property
     def shape(self):
@@ -66,7 +74,19 @@ WORKLOADS = {
     3: Workload(3, "vit_h16_n1024_d64", 16, 1024, 64, "normal"),
     4: Workload(4, "vit_ragged_h12_n4097_d32", 12, 4097, 32, "normal"),
     5: Workload(5, "vit_sharp_h128_n4096_d64", 128, 4096, 64, "sharp"),
+    6: Workload(6, "vit_sharp_patchmajor_h128_n4096_d64", 128, 4096, 64, "sharp", "patch"),
+    7: Workload(7, "vit_h16_n1024_d40", 16, 1024, 40, "normal"),
 }
+
+
+def to_layout(x, layout: str):
+    """A head-major [H][N][d] array in the storage order ``layout`` names
+    ("head": itself; "patch": a contiguous [N][H][d] copy)."""
+    if layout == "head":
+        return np.ascontiguousarray(x)
+    if layout == "patch":
+        return np.ascontiguousarray(np.transpose(x, (1, 0, 2)))
+    raise ValueError("unknown layout %r" % layout)
 
 
 def default_seed(wid: int) -> int:
