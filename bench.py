@@ -154,7 +154,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_heads": w.n_heads, "n_patches": w.n_patches,
                    "head_dim": w.head_dim, "precision": args.precision,
-                   "io": "f32 %s resident in HBM" % ("[N][H][d]" if w.layout == "patch" else "[H][N][d]")},
+                   "io": "%s %s resident in HBM" % (w.dtype, "[N][H][d]" if w.layout == "patch" else "[H][N][d]")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),

@@ -46,8 +46,9 @@ typedef enum vattn_status {
                                 / grid cannot address                        */
     VATTN_ERR_HEAD_DIM = 3,  /* head_dim is not in [1, 64]                   */
     VATTN_ERR_ALIGN = 4,     /* a tensor base address is not aligned for its
-                                access mode (16 bytes, or 4 bytes when
-                                head_dim or a stride is not a multiple of 4)  */
+                                access mode (4 elements: 16 bytes of f32 or
+                                8 of f16; one element when head_dim or a
+                                stride is not a multiple of 4)                */
     VATTN_ERR_ALIAS = 5,     /* out overlaps q, k or v                       */
     VATTN_ERR_HIP = 6,       /* the HIP runtime refused the launch           */
     VATTN_ERR_ARG = 7        /* unknown precision mode                       */
@@ -142,6 +143,24 @@ int vattn_forward_strided(const float *q, const float *k, const float *v,
                           float *out, int n_heads, int n_patches, int head_dim,
                           long long stride_head, long long stride_patch,
                           int precision, void *stream);
+
+/*
+ * vattn_forward_f16 - as vattn_forward_strided for IEEE binary16 (f16)
+ * tensors: q, k, v and out hold f16 values (2 bytes each, passed as void
+ * pointers since C has no standard half type).  No conversion is needed on
+ * the way to the matrix cores and HBM traffic halves.  Products of f16
+ * inputs are exact in the f32 accumulator, so the SPLIT/AUTO correction
+ * only adds q_lo.k (the query is scaled by log2(e) in f32 and split into
+ * two f16 parts).  The result is rounded to f16 (round-to-nearest-even).
+ * Strides count f16 elements.  Vector access needs 8-byte aligned bases;
+ * 2-byte alignment suffices when head_dim or a stride is not a multiple of
+ * 4.  Head-major tensors: stride_head = n_patches*head_dim, stride_patch =
+ * head_dim.  Errors and stream semantics as for vattn_forward_strided.
+ */
+int vattn_forward_f16(const void *q, const void *k, const void *v, void *out,
+                      int n_heads, int n_patches, int head_dim,
+                      long long stride_head, long long stride_patch,
+                      int precision, void *stream);
 
 /* Static, never-NULL description of a status code ("unknown status" for
  * values outside vattn_status). */

@@ -38,7 +38,7 @@ PRECISION = {"auto": 0, "fast": 1, "split": 2}
 
 # Symbols declared in include/vattn.h.
 EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_forward_strided",
-           "vattn_status_string", "vattn_last_hip_error")
+           "vattn_forward_f16", "vattn_status_string", "vattn_last_hip_error")
 
 
 class VattnError(RuntimeError):
@@ -64,6 +64,8 @@ def _load():
     ll = ctypes.c_longlong
     lib.vattn_forward_strided.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp]
     lib.vattn_forward_strided.restype = ci
+    lib.vattn_forward_f16.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp]
+    lib.vattn_forward_f16.restype = ci
     lib.vattn_status_string.argtypes = [ci]
     lib.vattn_status_string.restype = ctypes.c_char_p
     lib.vattn_last_hip_error.argtypes = []
@@ -97,6 +99,18 @@ def forward_strided_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_head
                                      mode, stream or None)
 
 
+def forward_f16_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
+                    n_patches: int, head_dim: int, stride_head: int, stride_patch: int,
+                    stream: int = 0, precision: str | int = "auto") -> int:
+    """Direct call of ``vattn_forward_f16`` (f16 tensors, strides in
+    elements); returns the status code."""
+    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    return lib.vattn_forward_f16(q_ptr or None, k_ptr or None, v_ptr or None,
+                                 out_ptr or None, int(n_heads), int(n_patches),
+                                 int(head_dim), int(stride_head), int(stride_patch),
+                                 mode, stream or None)
+
+
 def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
                   n_patches: int, head_dim: int, stream: int = 0) -> int:
     """Direct call of the C entry point ``vattn_forward``; returns its status."""
@@ -108,8 +122,8 @@ def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int
 def _check(t: torch.Tensor, name: str):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype != torch.float32:
-        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.dtype not in (torch.float32, torch.float16):
+        raise TypeError("%s must be float32 or float16, got %s" % (name, t.dtype))
     if t.device.type != "cuda":
         raise ValueError("%s must be on a HIP device" % name)
     if t.dim() != 3:
@@ -123,7 +137,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """out[h] = softmax(q[h] @ k[h]^T) @ v[h] for every head (no scale inside).
 
-    q, k, v, out: float32 [n_heads, n_patches, head_dim] on one device,
+    q, k, v, out: float32 (or all float16) [n_heads, n_patches, head_dim] on one device,
     head_dim <= 64, last dimension contiguous and the same strides for all
     four (contiguous head-major tensors, or e.g. patch-major [N, H, d]
     tensors viewed as ``x.transpose(0, 1)``).  ``out`` defaults to a new
@@ -131,12 +145,19 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     current stream); returns ``out`` without synchronising.
     """
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ: %s %s %s" % (q.dtype, k.dtype, v.dtype))
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, name)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v shapes differ: %s %s %s" % (q.shape, k.shape, v.shape))
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     _check(out, "out")
+    if out.dtype != q.dtype:
+        raise TypeError("out dtype %s != %s" % (out.dtype, q.dtype))
     if out.shape != q.shape:
         raise ValueError("out shape %s != %s" % (out.shape, q.shape))
     devs = {q.device, k.device, v.device, out.device}
@@ -149,7 +170,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sh, sn = strides.pop()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream()
-        if q.is_contiguous():
+        if q.dtype == torch.float16:
+            rc = forward_f16_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 h, n, d, sh, sn, s.cuda_stream, precision)
+        elif q.is_contiguous():
             rc = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              h, n, d, s.cuda_stream, precision)
         else:

@@ -105,9 +105,10 @@ struct Shape {
     static_assert(WAVES == 8 || WAVES == 16, "8 or 16 waves per workgroup");
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kBlockM = kRowsPerWave * WAVES;      // query rows per workgroup
-    static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) floats per thread
-    static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // floats per load
+    static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) elements per thread
+    static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // elements per load
     static constexpr int kKVec = kTileElems / kKWidth;        // loads per thread per tensor
+    static_assert(kKWidth == 2 || kKWidth == 4, "tile/thread shape");
 };
 
 // Dispatch places workgroup b on XCD b % 8.  Give each XCD a contiguous run
@@ -160,61 +161,52 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // guards and no address clamping in the vector ALUs.
 constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data, gfx9 descriptor layout
 
-template <int D, int IO>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *head, int key0,
+// Element type of the tensors in HBM: float (converted to f16 on the way
+// into LDS) or _Float16 (copied as is).
+template <typename T, int N>
+struct VecOf {
+    typedef T type __attribute__((ext_vector_type(N)));
+};
+
+template <int D, int IO, typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T *head, int key0,
                                                             int n_patches, const Io &io) {
     const int rows = max(n_patches - key0, 0);
     if constexpr (IO == kIoDense)
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(head + (size_t)key0 * D),
-                                                 (short)0, rows * D * (int)sizeof(float),
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(head + (size_t)key0 * D),
+                                                 (short)0, rows * D * (int)sizeof(T),
                                                  kBufferFlags);
     else
         return __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(head + (size_t)key0 * io.stride_patch), (short)0,
-            rows > 0 ? ((rows - 1) * io.stride_patch + io.head_dim) * (int)sizeof(float) : 0,
+            const_cast<T *>(head + (size_t)key0 * io.stride_patch), (short)0,
+            rows > 0 ? ((rows - 1) * io.stride_patch + io.head_dim) * (int)sizeof(T) : 0,
             kBufferFlags);
 }
 
-template <int N>
-struct FloatVec;
-template <>
-struct FloatVec<4> {
-    typedef float4_t type;
-    typedef half4_t half_type;
-};
-template <>
-struct FloatVec<2> {
-    typedef float2_t type;
-    typedef half2_t half_type;
-};
-template <>
-struct FloatVec<1> {
-    typedef float type;
-    typedef _Float16 half_type;
-};
-
-template <int N>
-__device__ __forceinline__ typename FloatVec<N>::type buf_load(__amdgpu_buffer_rsrc_t r,
-                                                               int byte_off) {
-    if constexpr (N == 4)
-        return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-    else if constexpr (N == 2)
-        return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+template <typename T, int N>
+__device__ __forceinline__ typename VecOf<T, N>::type buf_load_vec(__amdgpu_buffer_rsrc_t r,
+                                                                   int byte_off) {
+    typedef typename VecOf<T, N>::type V;
+    constexpr int kBytes = (int)sizeof(T) * N;
+    if constexpr (kBytes == 16)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    else if constexpr (kBytes == 8)
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
     else
-        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
-template <int N>
-__device__ __forceinline__ float elem(typename FloatVec<N>::type x, int j) {
-    if constexpr (N == 1)
-        return x;
+template <typename T>
+__device__ __forceinline__ T buf_load_one(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    if constexpr (sizeof(T) == 4)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
     else
-        return x[j];
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
 }
 
 // Per-thread part of the tile layout (the same for every tile): load u of
 // the thread covers f = tid + kThreads*u of the tile in units of kKWidth
-// floats, row f / (D/kKWidth), columns kKWidth*(f % ..), so a wave reads
+// elements, row f / (D/kKWidth), columns kKWidth*(f % ..), so a wave reads
 // whole rows.  K and V share the mapping.
 template <int D, int WAVES>
 struct TileMap {
@@ -228,39 +220,37 @@ struct TileMap {
     }
 };
 
-template <int D, int WAVES>
+template <int D, int WAVES, typename T>
 struct TileRegs {
     using S = Shape<D, WAVES>;
-    typename FloatVec<S::kKWidth>::type k[S::kKVec];
-    typename FloatVec<S::kKWidth>::type v[S::kKVec];
+    typename VecOf<T, S::kKWidth>::type k[S::kKVec];
+    typename VecOf<T, S::kKWidth>::type v[S::kKVec];
 };
 
-// Vector of N floats at columns [col, col+N) of a row: the strided modes
-// move columns >= head_dim out of the buffer range (read as 0).
-template <int N, int IO>
-__device__ __forceinline__ typename FloatVec<N>::type load_cols(__amdgpu_buffer_rsrc_t r,
+// Vector of N elements at columns [col, col+N) of a row (row_off = the
+// row's element offset): the strided modes move columns >= head_dim out of
+// the buffer range (read as 0).
+template <typename T, int N, int IO>
+__device__ __forceinline__ typename VecOf<T, N>::type load_cols(__amdgpu_buffer_rsrc_t r,
                                                                 int row_off, int col,
                                                                 const Io &io) {
+    constexpr int kSz = (int)sizeof(T);
     if constexpr (IO == kIoScalar) {
-        typename FloatVec<N>::type x;
-        if constexpr (N == 1) {
-            x = buf_load<1>(r, col < io.head_dim ? (row_off + col) * 4 : kOutOfRange);
-        } else {
+        typename VecOf<T, N>::type x;
 #pragma unroll
-            for (int j = 0; j < N; ++j)
-                x[j] = buf_load<1>(r, col + j < io.head_dim ? (row_off + col + j) * 4 : kOutOfRange);
-        }
+        for (int j = 0; j < N; ++j)
+            x[j] = buf_load_one<T>(r, col + j < io.head_dim ? (row_off + col + j) * kSz : kOutOfRange);
         return x;
     } else {
         const bool in = IO == kIoDense || col < io.head_dim;
-        return buf_load<N>(r, in ? (row_off + col) * 4 : kOutOfRange);
+        return buf_load_vec<T, N>(r, in ? (row_off + col) * kSz : kOutOfRange);
     }
 }
 
-template <int D, int WAVES, int IO>
-__device__ __forceinline__ void load_tile(const float *kg, const float *vg, int key0,
+template <int D, int WAVES, int IO, typename T>
+__device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
                                           int n_patches, const TileMap<D, WAVES> &m,
-                                          TileRegs<D, WAVES> &r, const Io &io) {
+                                          TileRegs<D, WAVES, T> &r, const Io &io) {
     using S = Shape<D, WAVES>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
@@ -268,28 +258,29 @@ __device__ __forceinline__ void load_tile(const float *kg, const float *vg, int 
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
         const int row_off = (m.row0 + u * TileMap<D, WAVES>::kRowStep) * pitch;
-        r.k[u] = load_cols<S::kKWidth, IO>(rk, row_off, m.col, io);
-        r.v[u] = load_cols<S::kKWidth, IO>(rv, row_off, m.col, io);
+        r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io);
+        r.v[u] = load_cols<T, S::kKWidth, IO>(rv, row_off, m.col, io);
     }
 }
 
-// Registers -> LDS, both row-major [key][dim] in f16 (RNE); SPLIT also
-// stores k_lo = f16(k - f32(f16(k))).
-template <int D, int WAVES, bool SPLIT>
-__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES> &r,
+// Registers -> LDS, both row-major [key][dim] in f16 (RNE from f32); with
+// f32 inputs SPLIT also stores k_lo = f16(k - f32(f16(k))).  f16 inputs
+// are exact in f16 (no k_lo).
+template <int D, int WAVES, bool SPLIT, typename T>
+__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
                                            _Float16 (*vh)[Lds<D>::kKRow],
                                            const TileMap<D, WAVES> &m) {
     using S = Shape<D, WAVES>;
-    typedef typename FloatVec<S::kKWidth>::type Vec;
-    typedef typename FloatVec<S::kKWidth>::half_type Half;
+    typedef typename VecOf<float, S::kKWidth>::type Vec;
+    typedef typename VecOf<_Float16, S::kKWidth>::type Half;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
         const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
         const Half hi = __builtin_convertvector(r.k[u], Half);
         *reinterpret_cast<Half *>(&kh[row][m.col]) = hi;
-        if constexpr (SPLIT) {
+        if constexpr (SPLIT && sizeof(T) == 4) {
             const Vec back = __builtin_convertvector(hi, Vec);
             *reinterpret_cast<Half *>(&kl[row][m.col]) = __builtin_convertvector(r.k[u] - back, Half);
         }
@@ -310,8 +301,9 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // lie above -lo_window relative to m_ref (lo_window = +inf: every block,
 // -inf: none).  A key whose f16 logit sits more than lo_window below the
 // running max has weight below 2^-lo_window, so the ~2^-11 relative error
-// its q_hi.k_hi logit carries is negligible in the output.
-template <int D, bool SPLIT>
+// its q_hi.k_hi logit carries is negligible in the output.  KLO = false
+// (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
+template <int D, bool SPLIT, bool KLO>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
                                         const half8_t (&qh)[Lds<D>::kKSteps],
@@ -335,10 +327,12 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                 for (int st = 0; st < Lds<D>::kKSteps; ++st) {
                     const half8_t a = *reinterpret_cast<const half8_t *>(
                         &kh[16 * kb + l16][32 * st + 8 * g4]);
-                    const half8_t al = *reinterpret_cast<const half8_t *>(
-                        &kl[16 * kb + l16][32 * st + 8 * g4]);
                     s[kb] = mfma16(a, ql[st], s[kb]);
-                    s[kb] = mfma16(al, qh[st], s[kb]);
+                    if constexpr (KLO) {
+                        const half8_t al = *reinterpret_cast<const half8_t *>(
+                            &kl[16 * kb + l16][32 * st + 8 * g4]);
+                        s[kb] = mfma16(al, qh[st], s[kb]);
+                    }
                 }
             }
         }
@@ -466,28 +460,29 @@ struct IntTag {
 // hides behind a whole tile of compute.  Matrix and vector work overlap
 // across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
-template <int D, int WAVES, bool SPLIT, int IO>
+template <int D, int WAVES, bool SPLIT, int IO, typename T>
 __global__ void __launch_bounds__(64 * WAVES, 4)
-attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
-                     const float *__restrict__ v, float *__restrict__ out,
+attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                     const T *__restrict__ v, T *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks, float lo_window,
                      float lo_gate, Io io) {
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
+    constexpr bool KLO = SPLIT && sizeof(T) == 4;  // k_lo tiles (f32 inputs only)
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
-    _Float16 kl_s[SPLIT ? 2 : 1][SPLIT ? kTileN : 1][L::kKRow];
+    _Float16 kl_s[KLO ? 2 : 1][KLO ? kTileN : 1][L::kKRow];
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
     const int qblk = logical - head * q_blocks;
     const size_t base = IO == kIoDense ? (size_t)head * (size_t)n_patches * D
                                        : (size_t)((long long)head * io.stride_head);
-    const float *__restrict__ qg = q + base;
-    const float *kg = k + base;
-    const float *vg = v + base;
-    float *__restrict__ og = out + base;
+    const T *__restrict__ qg = q + base;
+    const T *kg = k + base;
+    const T *vg = v + base;
+    T *__restrict__ og = out + base;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -507,15 +502,16 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     for (int st = 0; st < L::kKSteps; ++st) {
         float4_t x0 = zero4(), x1 = zero4();
         const int c = 32 * st + 8 * g4;
+        typedef typename VecOf<T, 4>::type T4;
         if constexpr (IO == kIoDense) {
             if (row < n_patches) {
-                const float *p = qg + row * D + c;
-                x0 = load4(p);
-                x1 = load4(p + 4);
+                const T *p = qg + row * D + c;
+                x0 = __builtin_convertvector(*reinterpret_cast<const T4 *>(p), float4_t);
+                x1 = __builtin_convertvector(*reinterpret_cast<const T4 *>(p + 4), float4_t);
             }
         } else if (row < n_patches) {
-            x0 = load_cols<4, IO>(rq, row * io.stride_patch, c, io);
-            x1 = load_cols<4, IO>(rq, row * io.stride_patch, c + 4, io);
+            x0 = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io), float4_t);
+            x1 = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c + 4, io), float4_t);
         }
         x0 *= kLog2e;
         x1 *= kLog2e;
@@ -530,9 +526,9 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
         }
     }
 
-    TileRegs<D, WAVES> regs;
+    TileRegs<D, WAVES, T> regs;
     load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
-    store_tile<D, WAVES, SPLIT>(regs, kh_s[0], kl_s[0], vt_s[0], map);
+    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map);
     if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
     __syncthreads();
 
@@ -550,8 +546,8 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
         // drain while this tile is computed, and the stores have landed long
         // before the barrier.
         if (t + 1 < n_tiles) {
-            store_tile<D, WAVES, SPLIT>(regs, kh_s[BUF ^ 1], kl_s[SPLIT ? (BUF ^ 1) : 0],
-                                        vt_s[BUF ^ 1], map);
+            store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
+                                           vt_s[BUF ^ 1], map);
             if (t + 2 < n_tiles)
                 load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
         }
@@ -564,7 +560,7 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
             if (m_run != -__builtin_inff())
                 win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
         }
-        qk_tile<D, SPLIT>(kh_s[BUF], kl_s[SPLIT ? BUF : 0], qh, ql, c0, s, l16, g4, win);
+        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, l16, g4, win);
         const int key_lim = n_patches - t * kTileN;
         if (key_lim < kTileN)
             softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
@@ -581,18 +577,20 @@ attention_fwd_kernel(const float *__restrict__ q, const float *__restrict__ k,
     // modes, columns below head_dim).
     const float inv = 1.0f / sum_lane_groups(l_run);
     if (row < n_patches) {
+        typedef typename VecOf<T, 4>::type T4;
         if constexpr (IO == kIoDense) {
 #pragma unroll
             for (int db = 0; db < L::kDBlocks; ++db)
-                *reinterpret_cast<float4_t *>(og + row * D + 16 * db + 4 * g4) = o[db] * inv;
+                *reinterpret_cast<T4 *>(og + row * D + 16 * db + 4 * g4) =
+                    __builtin_convertvector(o[db] * inv, T4);
         } else {
-            float *orow = og + (size_t)row * io.stride_patch;
+            T *orow = og + (size_t)row * io.stride_patch;
 #pragma unroll
             for (int db = 0; db < L::kDBlocks; ++db) {
                 const int c = 16 * db + 4 * g4;
-                const float4_t y = o[db] * inv;
+                const T4 y = __builtin_convertvector(o[db] * inv, T4);
                 if constexpr (IO == kIoVec4) {
-                    if (c < io.head_dim) *reinterpret_cast<float4_t *>(orow + c) = y;
+                    if (c < io.head_dim) *reinterpret_cast<T4 *>(orow + c) = y;
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)

@@ -37,8 +37,8 @@ struct SplitPolicy {
     float gate;
 };
 
-template <int D, int WAVES, bool SPLIT, int IO>
-hipError_t launch(const float *q, const float *k, const float *v, float *out,
+template <int D, int WAVES, bool SPLIT, int IO, typename T>
+hipError_t launch(const T *q, const T *k, const T *v, T *out,
                   int n_heads, int n_patches, SplitPolicy pol, vattn::Io io,
                   hipStream_t stream) {
     constexpr int kBlockM = vattn::Shape<D, WAVES>::kBlockM;
@@ -49,35 +49,35 @@ hipError_t launch(const float *q, const float *k, const float *v, float *out,
                     (void *)&total_blocks, (void *)&pol.window, (void *)&pol.gate,
                     (void *)&io};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT, IO>),
+        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT, IO, T>),
         dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, stream);
 }
 
 // 16-wave workgroups (256 query rows) share each K/V tile among twice the
 // queries, halving L2 traffic and conversion work per query; they run one per
 // CU.  Use them when they still give every CU at least one workgroup.
-template <int D, bool SPLIT, int IO>
-hipError_t launch_any(const float *q, const float *k, const float *v, float *out,
+template <int D, bool SPLIT, int IO, typename T>
+hipError_t launch_any(const T *q, const T *k, const T *v, T *out,
                       int n_heads, int n_patches, SplitPolicy pol, vattn::Io io,
                       hipStream_t stream) {
     const int64_t wide_blocks =
         (int64_t)n_heads * (((int64_t)n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
                             vattn::Shape<D, 16>::kBlockM);
     if (wide_blocks >= kCusPerDevice)
-        return launch<D, 16, SPLIT, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream);
-    return launch<D, 8, SPLIT, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream);
+        return launch<D, 16, SPLIT, IO, T>(q, k, v, out, n_heads, n_patches, pol, io, stream);
+    return launch<D, 8, SPLIT, IO, T>(q, k, v, out, n_heads, n_patches, pol, io, stream);
 }
 
-template <int D, int IO>
-hipError_t launch_mode(const float *q, const float *k, const float *v, float *out,
+template <int D, int IO, typename T>
+hipError_t launch_mode(const T *q, const T *k, const T *v, T *out,
                        int n_heads, int n_patches, bool split, SplitPolicy pol,
                        vattn::Io io, hipStream_t stream) {
     return split ? launch_any<D, true, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream)
                  : launch_any<D, false, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream);
 }
 
-template <int D>
-hipError_t launch_io(const float *q, const float *k, const float *v, float *out,
+template <int D, typename T>
+hipError_t launch_io(const T *q, const T *k, const T *v, T *out,
                      int n_heads, int n_patches, bool split, SplitPolicy pol, vattn::Io io,
                      int mode, hipStream_t stream) {
     if (mode == vattn::kIoDense)
@@ -87,28 +87,11 @@ hipError_t launch_io(const float *q, const float *k, const float *v, float *out,
     return launch_mode<D, vattn::kIoScalar>(q, k, v, out, n_heads, n_patches, split, pol, io, stream);
 }
 
-}  // namespace
-
-extern "C" const char *vattn_status_string(int status) {
-    switch (status) {
-        case VATTN_OK: return "ok";
-        case VATTN_ERR_NULL: return "null tensor pointer";
-        case VATTN_ERR_SIZE: return "invalid or too large size or stride";
-        case VATTN_ERR_HEAD_DIM: return "head_dim must be in [1, 64]";
-        case VATTN_ERR_ALIGN: return "tensor not aligned for its access mode";
-        case VATTN_ERR_ALIAS: return "out overlaps q, k or v";
-        case VATTN_ERR_HIP: return "HIP runtime error";
-        case VATTN_ERR_ARG: return "unknown precision mode";
-        default: return "unknown status";
-    }
-}
-
-extern "C" int vattn_last_hip_error(void) { return g_last_hip_error; }
-
-extern "C" int vattn_forward_strided(const float *q, const float *k, const float *v,
-                                     float *out, int n_heads, int n_patches,
-                                     int head_dim, long long stride_head,
-                                     long long stride_patch, int precision, void *stream) {
+// Checks and dispatch shared by the f32 and f16 entry points.
+template <typename T>
+int forward_impl(const T *q, const T *k, const T *v, T *out, int n_heads, int n_patches,
+                 int head_dim, long long stride_head, long long stride_patch, int precision,
+                 void *stream) {
     if (n_heads < 0 || n_patches < 0) return VATTN_ERR_SIZE;
     if (head_dim < 1 || head_dim > 64) return VATTN_ERR_HEAD_DIM;
     if (precision != VATTN_PRECISION_AUTO && precision != VATTN_PRECISION_FAST &&
@@ -139,11 +122,13 @@ extern "C" int vattn_forward_strided(const float *q, const float *k, const float
     else
         mode = vattn::kIoScalar;
 
+    // Vector modes move 4-element vectors (16 bytes of f32, 8 of f16).
+    const uintptr_t align = mode == vattn::kIoScalar ? sizeof(T) : 4 * sizeof(T);
     const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
-    if (mis & (mode == vattn::kIoScalar ? 3u : 15u)) return VATTN_ERR_ALIGN;
+    if (mis & (align - 1)) return VATTN_ERR_ALIGN;
 
-    const uintptr_t bytes = (uintptr_t)(((H - 1) * sh + (N - 1) * sn + d) * (int64_t)sizeof(float));
+    const uintptr_t bytes = (uintptr_t)(((H - 1) * sh + (N - 1) * sn + d) * (int64_t)sizeof(T));
     const uintptr_t po = reinterpret_cast<uintptr_t>(out);
     if (overlaps(po, bytes, reinterpret_cast<uintptr_t>(q), bytes) ||
         overlaps(po, bytes, reinterpret_cast<uintptr_t>(k), bytes) ||
@@ -166,6 +151,42 @@ extern "C" int vattn_forward_strided(const float *q, const float *k, const float
         return VATTN_ERR_HIP;
     }
     return VATTN_OK;
+}
+
+}  // namespace
+
+extern "C" const char *vattn_status_string(int status) {
+    switch (status) {
+        case VATTN_OK: return "ok";
+        case VATTN_ERR_NULL: return "null tensor pointer";
+        case VATTN_ERR_SIZE: return "invalid or too large size or stride";
+        case VATTN_ERR_HEAD_DIM: return "head_dim must be in [1, 64]";
+        case VATTN_ERR_ALIGN: return "tensor not aligned for its access mode";
+        case VATTN_ERR_ALIAS: return "out overlaps q, k or v";
+        case VATTN_ERR_HIP: return "HIP runtime error";
+        case VATTN_ERR_ARG: return "unknown precision mode";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int vattn_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int vattn_forward_strided(const float *q, const float *k, const float *v,
+                                     float *out, int n_heads, int n_patches,
+                                     int head_dim, long long stride_head,
+                                     long long stride_patch, int precision, void *stream) {
+    return forward_impl<float>(q, k, v, out, n_heads, n_patches, head_dim, stride_head,
+                               stride_patch, precision, stream);
+}
+
+extern "C" int vattn_forward_f16(const void *q, const void *k, const void *v, void *out,
+                                 int n_heads, int n_patches, int head_dim,
+                                 long long stride_head, long long stride_patch,
+                                 int precision, void *stream) {
+    return forward_impl<_Float16>(static_cast<const _Float16 *>(q), static_cast<const _Float16 *>(k),
+                                  static_cast<const _Float16 *>(v), static_cast<_Float16 *>(out),
+                                  n_heads, n_patches, head_dim, stride_head, stride_patch,
+                                  precision, stream);
 }
 
 extern "C" int vattn_forward_precision(const float *q, const float *k,

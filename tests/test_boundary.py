@@ -127,6 +127,25 @@ def test_scalar_mode_accepts_4_byte_alignment():
     assert vattn.forward_strided_raw(A + 4, B, C, O, H, N, 41, N * 41, 41) == vattn.VATTN_ERR_HIP
 
 
+@pytest.mark.parametrize("args,offset,status", [
+    # f16: vectors of 4 elements need 8-byte alignment; odd shapes only 2 bytes
+    ((H, N, 64, N * 64, 64), 4, vattn.VATTN_ERR_ALIGN),
+    ((H, N, 64, N * 64, 64), 2, vattn.VATTN_ERR_ALIGN),
+    ((H, N, 41, N * 41, 41), 1, vattn.VATTN_ERR_ALIGN),
+    ((H, N, 65, N * 65, 65), 0, vattn.VATTN_ERR_HEAD_DIM),
+    ((H, N, 64, 64, 64), 0, vattn.VATTN_ERR_SIZE),
+])
+def test_f16_validation(args, offset, status):
+    assert vattn.forward_f16_raw(A + offset, B, C, O, *args) == status
+
+
+def test_f16_reaches_launch_with_8_byte_alignment():
+    if torch.cuda.is_available():
+        pytest.skip("launch would run on the GPU")
+    assert vattn.forward_f16_raw(A + 8, B, C, O, H, N, 64, N * 64, 64) == vattn.VATTN_ERR_HIP
+    assert vattn.forward_f16_raw(A + 2, B, C, O, H, N, 41, N * 41, 41) == vattn.VATTN_ERR_HIP
+
+
 def test_unknown_precision_mode():
     assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, 3) == vattn.VATTN_ERR_ARG
     assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, -1) == vattn.VATTN_ERR_ARG
@@ -153,5 +172,7 @@ def test_python_wrapper_rejects_bad_tensors():
         vattn.forward(x, x, x)  # CPU tensors
     with pytest.raises(TypeError):
         vattn.forward(x.double(), x, x)
+    with pytest.raises(TypeError):
+        vattn.forward(x.half(), x, x)  # mixed dtypes
     with pytest.raises(ValueError):
         vattn.forward(x, x, x.transpose(1, 2).contiguous().transpose(1, 2))  # strided last dim

@@ -23,10 +23,14 @@ id    H       N       d         distribution
                                 (16 heads x 8 images; sharp softmax)
 6     128     4096    64        as 5, stored patch-major [N][H][d]
 7     16      1024    40        Q ~ N(0,1)/sqrt(40), K, V ~ N(0,1) (head_dim 40)
+8     16      1024    64        as 3, stored as f16
+9     128     4096    64        as 5, stored as f16
 ====  ======  ======  ========  ===================================================
 
-Workloads 1-5 are the head-major [H][N][d] cases; 6 and 7 exercise the
-strided (patch-major) access and a head_dim that is neither 32 nor 64.
+Workloads 1-5 are the head-major f32 [H][N][d] cases; 6 and 7 exercise the
+strided (patch-major) access and a head_dim that is neither 32 nor 64; 8
+and 9 the f16 tensors (the f32 draws rounded to f16, round-to-nearest-even;
+both sides then see the same f16 values).
 ``make_inputs`` always returns head-major arrays; ``to_layout`` gives the
 storage order a workload is run in.
 
@@ -48,6 +52,7 @@ class Workload:
     head_dim: int
     kind: str  # "normal" or "sharp"
     layout: str = "head"  # "head": [H][N][d]; "patch": [N][H][d]
+    dtype: str = "f32"    # element type in HBM: "f32" or "f16"
 
     @property
     def shape(self):
@@ -60,8 +65,10 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """f32 Q, K, V read once and out written once: 16*H*N*d bytes."""
-        return 16 * self.n_heads * self.n_patches * self.head_dim
+        """Q, K, V read once and out written once: 4 * H*N*d elements (16 bytes
+        per element quad for f32, 8 for f16)."""
+        elem = 2 if self.dtype == "f16" else 4
+        return 4 * elem * self.n_heads * self.n_patches * self.head_dim
 
     def describe(self) -> str:
         return "%s (H=%d, N=%d, d=%d)" % (self.name, self.n_heads,
@@ -76,6 +83,8 @@ WORKLOADS = {
     5: Workload(5, "vit_sharp_h128_n4096_d64", 128, 4096, 64, "sharp"),
     6: Workload(6, "vit_sharp_patchmajor_h128_n4096_d64", 128, 4096, 64, "sharp", "patch"),
     7: Workload(7, "vit_h16_n1024_d40", 16, 1024, 40, "normal"),
+    8: Workload(8, "vit_f16_h16_n1024_d64", 16, 1024, 64, "normal", dtype="f16"),
+    9: Workload(9, "vit_f16_sharp_h128_n4096_d64", 128, 4096, 64, "sharp", dtype="f16"),
 }
 
 
@@ -94,7 +103,8 @@ def default_seed(wid: int) -> int:
 
 
 def make_inputs(wid: int, seed: int | None = None, n_heads: int | None = None):
-    """Q, K, V float32 arrays of workload ``wid``.
+    """Q, K, V arrays of workload ``wid`` (float32, or float16 for the f16
+    workloads).
 
     ``n_heads`` (optional) draws only the first heads of the workload's
     stream shape-wise, i.e. a workload with fewer heads but the same
@@ -103,8 +113,11 @@ def make_inputs(wid: int, seed: int | None = None, n_heads: int | None = None):
     """
     w = WORKLOADS[wid]
     h = w.n_heads if n_heads is None else int(n_heads)
-    return make_custom(h, w.n_patches, w.head_dim, w.kind,
-                       default_seed(wid) if seed is None else seed)
+    q, k, v = make_custom(h, w.n_patches, w.head_dim, w.kind,
+                          default_seed(wid) if seed is None else seed)
+    if w.dtype == "f16":
+        q, k, v = (x.astype(np.float16) for x in (q, k, v))
+    return q, k, v
 
 
 def make_custom(n_heads: int, n_patches: int, head_dim: int,
