@@ -15,6 +15,13 @@
  * implementation choices of a fast kernel; the definition it approximates is
  * written out here directly, in float64, with no blocking or reordering.
  *
+ * The optional rotary position transform of Q and K follows the docs.rs page
+ * "rullama 0.2.0", src/kernels/wgsl/rope_neox_backward.wgsl: the forward
+ * NeoX rotation its header comment states (pairs x[i], x[i + rope_dims/2])
+ * and the angle pos * base^(-2i/rope_dims), divided by factors[i] when
+ * factors are given, that its main function computes.  Here every patch
+ * has its own position, pos_offset + patch index.
+ *
  * Built with gcc (C99 + OpenMP); no GPU code, no shared headers with the
  * GPU library.
  */
@@ -28,15 +35,15 @@
 
 /* One query row: q_row[d] against the head's keys/values k_head, v_head
  * ([n][d] each).  s is caller scratch of n doubles.  Writes out_row[d]. */
-static void attend_row(const float *q_row, const float *k_head,
-                       const float *v_head, long n, long d, double *s,
+static void attend_row(const double *q_row, const double *k_head,
+                       const double *v_head, long n, long d, double *s,
                        double *out_row)
 {
-    /* logits s_j = q . k_j  (exact float32 -> float64 promotion) */
+    /* logits s_j = q . k_j */
     for (long j = 0; j < n; ++j) {
         double acc = 0.0;
         for (long c = 0; c < d; ++c)
-            acc += (double)q_row[c] * (double)k_head[j * d + c];
+            acc += q_row[c] * k_head[j * d + c];
         s[j] = acc;
     }
     /* row maximum */
@@ -53,11 +60,11 @@ static void attend_row(const float *q_row, const float *k_head,
     for (long c = 0; c < d; ++c) out_row[c] = 0.0;
     for (long j = 0; j < n; ++j)
         for (long c = 0; c < d; ++c)
-            out_row[c] += s[j] * (double)v_head[j * d + c];
+            out_row[c] += s[j] * v_head[j * d + c];
     for (long c = 0; c < d; ++c) out_row[c] /= l;
 }
 
-static int run_rows(const float *q, const float *k, const float *v,
+static int run_rows(const double *q, const double *k, const double *v,
                     long n_heads, long n_patches, long head_dim,
                     const long *rows, long n_rows, double *out,
                     int n_threads)
@@ -99,7 +106,7 @@ static int run_rows(const float *q, const float *k, const float *v,
     return status;
 }
 
-int vattn_oracle_f64(const float *q, const float *k, const float *v,
+int vattn_oracle_f64(const double *q, const double *k, const double *v,
                      double *out, long n_heads, long n_patches,
                      long head_dim, int n_threads)
 {
@@ -108,7 +115,7 @@ int vattn_oracle_f64(const float *q, const float *k, const float *v,
                     n_heads * n_patches, out, n_threads);
 }
 
-int vattn_oracle_rows_f64(const float *q, const float *k, const float *v,
+int vattn_oracle_rows_f64(const double *q, const double *k, const double *v,
                           long n_heads, long n_patches, long head_dim,
                           const long *rows, long n_rows, double *out_rows,
                           int n_threads)
@@ -116,4 +123,37 @@ int vattn_oracle_rows_f64(const float *q, const float *k, const float *v,
     if (n_rows > 0 && !rows) return -1;
     return run_rows(q, k, v, n_heads, n_patches, head_dim, rows, n_rows,
                     out_rows, n_threads);
+}
+
+int vattn_oracle_rope_f64(const double *x, double *y, long n_heads,
+                          long n_patches, long head_dim, long rope_dims,
+                          double base, const double *factors,
+                          long pos_offset)
+{
+    if (n_heads < 0 || n_patches < 0 || head_dim < 0 || pos_offset < 0)
+        return -1;
+    if (rope_dims < 0 || rope_dims > head_dim || rope_dims % 2 != 0)
+        return -1;
+    if (n_heads * n_patches * head_dim == 0) return 0;
+    if (!x || !y) return -1;
+    const long half = rope_dims / 2;
+    for (long h = 0; h < n_heads; ++h) {
+        for (long n = 0; n < n_patches; ++n) {
+            const double *xr = x + (h * n_patches + n) * head_dim;
+            double *yr = y + (h * n_patches + n) * head_dim;
+            for (long c = 0; c < head_dim; ++c) yr[c] = xr[c];
+            const double pos = (double)(pos_offset + n);
+            for (long i = 0; i < half; ++i) {
+                double theta = pos * pow(base, -2.0 * (double)i / (double)rope_dims);
+                if (factors) theta = theta / factors[i];
+                const double cs = cos(theta);
+                const double sn = sin(theta);
+                const double a = xr[i];
+                const double b = xr[i + half];
+                yr[i] = a * cs - b * sn;
+                yr[i + half] = a * sn + b * cs;
+            }
+        }
+    }
+    return 0;
 }

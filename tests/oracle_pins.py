@@ -299,3 +299,127 @@ ALL_PINS = [
     pin_key_shift_invariance,
     pin_output_in_value_hull,
 ]
+
+
+# ------------------------------------------------------------ rotary transform
+# Pins of the NeoX rotary transform (docs.rs page "rullama 0.2.0",
+# src/kernels/wgsl/rope_neox_backward.wgsl: forward rotation in its header
+# comment, angle pos * base^(-2i/rope_dims) [/ factors[i]] in its main
+# function).  Each ``rope_pin_*`` takes ``rope(x, rope_dims, base, factors,
+# pos_offset) -> float64 [H][N][d]`` (patch n at position pos_offset + n) and
+# ``attn`` as above.
+
+def _decimal_angles(n_patches, pos_offset):
+    """base 10000 and rope_dims 8 make the frequencies exact powers of ten:
+    10000^(-2i/8) = 10^-i, so theta[n, i] = (pos_offset + n) * 10^-i."""
+    pos = np.arange(n_patches, dtype=np.float64) + pos_offset
+    return pos[:, None] * np.array([1.0, 0.1, 0.01, 0.001])[None, :]
+
+
+def rope_pin_position_zero_is_identity(rope, attn):
+    """Every angle is 0 at position 0: the first patch is unchanged."""
+    x = _rng(40).standard_normal((2, 3, 12))
+    y = rope(x, 12, 10000.0, None, 0)
+    if not np.array_equal(y[:, 0], x[:, 0]):
+        raise AssertionError("position 0 changed the row")
+
+
+def rope_pin_decimal_frequencies(rope, attn):
+    """Pairs (i, i+4) of rope_dims 8 with base 10000 turn by (pos)*10^-i,
+    written as a complex product (x_i + j x_{i+4}) e^{j theta}; the two
+    dimensions past rope_dims pass through."""
+    x = _rng(41).standard_normal((2, 9, 10))
+    y = rope(x, 8, 10000.0, None, 5)
+    theta = _decimal_angles(9, 5)
+    z = (x[:, :, 0:4] + 1j * x[:, :, 4:8]) * np.exp(1j * theta)[None]
+    _close(y[:, :, 0:4], z.real, 1e-13, "rotated first halves")
+    _close(y[:, :, 4:8], z.imag, 1e-13, "rotated second halves")
+    if not np.array_equal(y[:, :, 8:], x[:, :, 8:]):
+        raise AssertionError("dimensions past rope_dims changed")
+
+
+def rope_pin_unit_vector_traces_the_angle(rope, attn):
+    """x = e_0 at position p turns into (cos p, sin p) in dims (0, half):
+    the lowest frequency is base^0 = 1 for every base."""
+    x = np.zeros((1, 7, 6))
+    x[:, :, 0] = 1.0
+    y = rope(x, 6, 37.5, None, 0)
+    for p in range(7):
+        _close(y[0, p], [math.cos(p), 0, 0, math.sin(p), 0, 0], 1e-15, "e_0 at %d" % p)
+
+
+def rope_pin_page_backward_inverts(rope, attn):
+    """The page's backward step (rotation by -theta: dx_i c + dx_{i+h} s,
+    -dx_i s + dx_{i+h} c) undoes the forward rotation exactly."""
+    x = _rng(42).standard_normal((3, 6, 8))
+    y = rope(x, 8, 10000.0, None, 11)
+    theta = _decimal_angles(6, 11)[None]
+    c, s = np.cos(theta), np.sin(theta)
+    a, b = y[:, :, 0:4], y[:, :, 4:8]
+    back = np.concatenate([a * c + b * s, -a * s + b * c], axis=2)
+    _close(back, x, 1e-13, "backward(forward(x))")
+
+
+def rope_pin_factors_divide_angles(rope, attn):
+    """factors 10^-i cancel the decimal frequencies: every pair turns by pos."""
+    x = _rng(43).standard_normal((2, 5, 8))
+    y = rope(x, 8, 10000.0, np.array([1.0, 0.1, 0.01, 0.001]), 3)
+    pos = (np.arange(5) + 3.0)[None, :, None]
+    z = (x[:, :, 0:4] + 1j * x[:, :, 4:8]) * np.exp(1j * pos)
+    _close(y[:, :, 0:4], z.real, 1e-13, "first halves")
+    _close(y[:, :, 4:8], z.imag, 1e-13, "second halves")
+
+
+def rope_pin_pair_norms_and_passthrough(rope, attn):
+    """A rotation keeps |(x_i, x_{i+h})| for every pair and leaves the rest."""
+    x = _rng(44).standard_normal((2, 40, 24))
+    y = rope(x, 16, 523.0, np.linspace(0.5, 4.0, 8), 2)
+    nx = x[:, :, 0:8] ** 2 + x[:, :, 8:16] ** 2
+    ny = y[:, :, 0:8] ** 2 + y[:, :, 8:16] ** 2
+    _close(ny, nx, 1e-12, "pair norms")
+    if not np.array_equal(y[:, :, 16:], x[:, :, 16:]):
+        raise AssertionError("dimensions past rope_dims changed")
+    if np.allclose(y[:, 1:, 0:16], x[:, 1:, 0:16]):
+        raise AssertionError("nothing was rotated")
+
+
+def rope_pin_relative_positions(rope, attn):
+    """Rotating queries and keys by their positions makes every logit depend
+    on the position difference only: shifting all positions leaves the
+    attention output unchanged."""
+    r = _rng(45)
+    q = r.standard_normal((2, 30, 16)) * 0.8
+    k = r.standard_normal((2, 30, 16)) * 0.8
+    v = r.standard_normal((2, 30, 16))
+    a = attn(rope(q, 16, 100.0, None, 0), rope(k, 16, 100.0, None, 0), v)
+    b = attn(rope(q, 16, 100.0, None, 97), rope(k, 16, 100.0, None, 97), v)
+    _close(a, b, 1e-11, "shifted positions")
+    c = attn(q, k, v)
+    if np.allclose(a, c, atol=1e-3):
+        raise AssertionError("rotation had no effect on attention")
+
+
+def rope_pin_attention_closed_form(rope, attn):
+    """head_dim 2, rope_dims 2: q = k = (a, 0) at every position p rotate to
+    a (cos p, sin p), so the logit of query p and key p' is a^2 cos(p - p')
+    and the output is the softmax of those logits applied to V."""
+    n, a = 12, 1.7
+    x = np.zeros((1, n, 2))
+    x[0, :, 0] = a
+    v = _rng(46).standard_normal((1, n, 2))
+    out = attn(rope(x, 2, 10000.0, None, 0), rope(x, 2, 10000.0, None, 0), v)
+    p = np.arange(n, dtype=np.float64)
+    logits = a * a * np.cos(p[:, None] - p[None, :])
+    _close(out[0], softmax(logits, axis=1) @ v[0], 1e-13, "closed-form logits")
+
+
+ROPE_PINS = [
+    rope_pin_position_zero_is_identity,
+    rope_pin_decimal_frequencies,
+    rope_pin_unit_vector_traces_the_angle,
+    rope_pin_page_backward_inverts,
+    rope_pin_factors_divide_angles,
+    rope_pin_pair_norms_and_passthrough,
+    rope_pin_relative_positions,
+    rope_pin_attention_closed_form,
+]
