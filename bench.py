@@ -7,6 +7,10 @@ query row) on inputs already resident in HBM.  Prints one JSON line with the
 attention throughput 4*H*N^2*d / time, the roofline of the kernel against
 the dense f16 matrix-core peak, and the float64 CPU oracle timed on a bounded
 sample of the same workload on the host's cores.
+
+Rotary workloads build their (cos, sin) table once, before timing (it
+depends on the positions only, like a weight); a step is then one
+``vattn_forward_rope``, which rotates Q and K inside the kernel.
 """
 from __future__ import annotations
 
@@ -54,16 +58,27 @@ def read_traffic(workload_name: str):
         return None
 
 
+def oracle_path(q, k, v, w, n_threads: int = 0, rows=None):
+    """The whole path in the float64 oracle: rotary transform of Q and K (for
+    the rotary workloads), then attention (all rows, or the listed rows)."""
+    import oracle
+    if w.rope_dims:
+        q = oracle.rope_neox_f64(q, w.rope_dims, w.rope_base)
+        k = oracle.rope_neox_f64(k, w.rope_dims, w.rope_base)
+    if rows is None:
+        return oracle.attention_f64(q, k, v, n_threads=n_threads)
+    return oracle.attention_rows_f64(q, k, v, rows, n_threads=n_threads)
+
+
 def cpu_baseline(q, k, v, w, target_s: float):
     """The float64 oracle, untuned, on the first heads of the workload."""
-    import oracle
     cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
     t0 = time.perf_counter()
-    oracle.attention_f64(q[:1], k[:1], v[:1], n_threads=cores)
+    oracle_path(q[:1], k[:1], v[:1], w, n_threads=cores)
     t1 = time.perf_counter() - t0
     heads = max(1, min(w.n_heads, int(round(target_s / max(t1, 1e-3)))))
     t0 = time.perf_counter()
-    oracle.attention_f64(q[:heads], k[:heads], v[:heads], n_threads=cores)
+    oracle_path(q[:heads], k[:heads], v[:heads], w, n_threads=cores)
     dt = time.perf_counter() - t0
     flops = 4.0 * heads * w.n_patches ** 2 * w.head_dim
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
@@ -106,16 +121,17 @@ def main():
     if w.layout == "patch":
         dq, dk, dv, out = (t.transpose(0, 1) for t in (dq, dk, dv, out))
     stream = torch.cuda.current_stream()
+    table = vattn.rope_table(w.n_patches, w.rope_dims, w.rope_base) if w.rope_dims else None
 
     for _ in range(args.warmup):
-        vattn.forward(dq, dk, dv, out=out, precision=args.precision)
+        vattn.forward(dq, dk, dv, out=out, precision=args.precision, rope=table)
     torch.cuda.synchronize()
 
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        vattn.forward(dq, dk, dv, out=out, precision=args.precision)
+        vattn.forward(dq, dk, dv, out=out, precision=args.precision, rope=table)
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -129,10 +145,9 @@ def main():
         torch.cuda.synchronize()
 
     # spot parity on sampled rows (not timed)
-    import oracle
     rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=2)
     got = out.contiguous().cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
-    ref = oracle.attention_rows_f64(q, k, v, rows)
+    ref = oracle_path(q, k, v, w, rows=rows)
     diff = got - ref
     parity = {"rows": int(rows.size), "max_abs": float(np.max(np.abs(diff))),
               "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
@@ -154,6 +169,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_heads": w.n_heads, "n_patches": w.n_patches,
                    "head_dim": w.head_dim, "precision": args.precision,
+                   "rope": ("NeoX rope_dims %d base %g, table built once" % (w.rope_dims, w.rope_base))
+                           if w.rope_dims else None,
                    "io": "%s %s resident in HBM" % (w.dtype, "[N][H][d]" if w.layout == "patch" else "[H][N][d]")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",

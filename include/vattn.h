@@ -51,7 +51,9 @@ typedef enum vattn_status {
                                 stride is not a multiple of 4)                */
     VATTN_ERR_ALIAS = 5,     /* out overlaps q, k or v                       */
     VATTN_ERR_HIP = 6,       /* the HIP runtime refused the launch           */
-    VATTN_ERR_ARG = 7        /* unknown precision mode                       */
+    VATTN_ERR_ARG = 7,       /* unknown precision mode                       */
+    VATTN_ERR_ROPE = 8       /* invalid rotary parameters (rope_dims, base,
+                                factors, positions)                          */
 } vattn_status;
 
 /* How the logits q.k are formed on the matrix cores.
@@ -161,6 +163,76 @@ int vattn_forward_f16(const void *q, const void *k, const void *v, void *out,
                       int n_heads, int n_patches, int head_dim,
                       long long stride_head, long long stride_patch,
                       int precision, void *stream);
+
+/*
+ * Rotary position transform of Q and K (NeoX pairing).  Source: docs.rs page
+ * "rullama 0.2.0", src/kernels/wgsl/rope_neox_backward.wgsl - the forward
+ * rotation its header comment states and the angle its main function
+ * computes.  For rope_dims <= head_dim and half = rope_dims / 2, the row of
+ * a patch at position pos turns its pairs (x[i], x[i + half]), i < half:
+ *
+ *     theta       = pos * base^(-2 i / rope_dims)  [ / factors[i] ]
+ *     x[i]        <- x[i] cos theta - x[i + half] sin theta
+ *     x[i + half] <- x[i] sin theta + x[i + half] cos theta
+ *
+ * and leaves dimensions >= rope_dims unchanged.  The page rotates the rows
+ * of one position; here every patch has its own position (1-D patch order).
+ */
+
+/*
+ * vattn_rope_table - enqueue the (cos, sin) table of the rotary angles.
+ *
+ * table       : device pointer, float32 [n_positions][rope_dims/2][2], fully
+ *               written: table[n][i] = (cos theta, sin theta) for position
+ *               pos = pos_offset + n and pair i.  theta, cos and sin are
+ *               evaluated in float64 and rounded to float32 (nearest).
+ *               16-byte aligned (VATTN_ERR_ALIGN).
+ * n_positions : >= 0 (0: nothing to do, table may be NULL); with rope_dims/2
+ *               entries per row, n_positions * rope_dims/2 < 2^31.
+ * rope_dims   : even, 2 ... 64.
+ * base        : finite and > 0 (the page's frequency base, e.g. 10000).
+ * factors     : HOST pointer to rope_dims/2 finite values > 0 that divide the
+ *               angles (the page's optional factors buffer), or NULL; read
+ *               during the call only.
+ * pos_offset  : position of row 0, >= 0; pos_offset + n_positions - 1 must fit
+ *               an int.
+ * Errors: VATTN_ERR_ROPE (rope_dims, base, factors, positions), VATTN_ERR_SIZE
+ * (n_positions), VATTN_ERR_NULL, VATTN_ERR_ALIGN, VATTN_ERR_HIP; checked
+ * synchronously, nothing enqueued on error.  No allocation.
+ */
+int vattn_rope_table(float *table, int n_positions, int rope_dims, float base,
+                     const float *factors, int pos_offset, void *stream);
+
+/*
+ * vattn_forward_rope - vattn_forward_strided with the rotary transform
+ * applied to q and k (not v) inside the kernel: out = softmax(rot(Q)
+ * rot(K)^T) V, where row i of every head is rotated with table row i (the
+ * position of patch i).  The rotation is done in f32 before the f16
+ * rounding; the rotated tensors are never written to memory and q, k stay
+ * unchanged.
+ *
+ * rope_dims  : multiple of 8, 8 ... head_dim (VATTN_ERR_ROPE otherwise).
+ * rope_table : device pointer to a table from vattn_rope_table with the same
+ *              rope_dims and at least n_patches rows (not checked), 16-byte
+ *              aligned; read only.  out must not overlap its first n_patches
+ *              rows (VATTN_ERR_ALIAS).
+ * Every other argument, error and the stream semantics as for
+ * vattn_forward_strided.  With f16 tensors the rotated K is not exact in f16,
+ * so SPLIT / AUTO also correct with q_hi.k_lo, as for f32 inputs.
+ */
+int vattn_forward_rope(const float *q, const float *k, const float *v,
+                       float *out, int n_heads, int n_patches, int head_dim,
+                       long long stride_head, long long stride_patch,
+                       int rope_dims, const float *rope_table, int precision,
+                       void *stream);
+
+/* vattn_forward_rope for f16 tensors (as vattn_forward_f16); the table stays
+ * float32. */
+int vattn_forward_rope_f16(const void *q, const void *k, const void *v,
+                           void *out, int n_heads, int n_patches, int head_dim,
+                           long long stride_head, long long stride_patch,
+                           int rope_dims, const float *rope_table,
+                           int precision, void *stream);
 
 /* Static, never-NULL description of a status code ("unknown status" for
  * values outside vattn_status). */

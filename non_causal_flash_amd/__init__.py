@@ -11,7 +11,12 @@ library is missing, importing this package raises.
 ``q``, ``k``, ``v`` (and ``out``) may also be strided views with the same
 strides and a contiguous last dimension, e.g. a patch-major ``[N, H, d]``
 tensor seen as ``x.transpose(0, 1)``; those go through
-``vattn_forward_strided``.
+``vattn_forward_strided``.  float16 tensors go through ``vattn_forward_f16``.
+
+With a rotary table (``rope_table(n_patches, rope_dims, base)``, built once
+per set of positions), ``forward(q, k, v, rope=table)`` rotates Q and K
+(NeoX pairs) inside the kernel: ``vattn_forward_rope`` /
+``vattn_forward_rope_f16``.
 """
 from __future__ import annotations
 
@@ -33,12 +38,14 @@ VATTN_ERR_ALIGN = 4
 VATTN_ERR_ALIAS = 5
 VATTN_ERR_HIP = 6
 VATTN_ERR_ARG = 7
+VATTN_ERR_ROPE = 8
 
 PRECISION = {"auto": 0, "fast": 1, "split": 2}
 
 # Symbols declared in include/vattn.h.
 EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_forward_strided",
-           "vattn_forward_f16", "vattn_status_string", "vattn_last_hip_error")
+           "vattn_forward_f16", "vattn_rope_table", "vattn_forward_rope",
+           "vattn_forward_rope_f16", "vattn_status_string", "vattn_last_hip_error")
 
 
 class VattnError(RuntimeError):
@@ -66,6 +73,12 @@ def _load():
     lib.vattn_forward_strided.restype = ci
     lib.vattn_forward_f16.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp]
     lib.vattn_forward_f16.restype = ci
+    lib.vattn_rope_table.argtypes = [vp, ci, ci, ctypes.c_float, vp, ci, vp]
+    lib.vattn_rope_table.restype = ci
+    lib.vattn_forward_rope.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp, ci, vp]
+    lib.vattn_forward_rope.restype = ci
+    lib.vattn_forward_rope_f16.argtypes = [vp, vp, vp, vp, ci, ci, ci, ll, ll, ci, vp, ci, vp]
+    lib.vattn_forward_rope_f16.restype = ci
     lib.vattn_status_string.argtypes = [ci]
     lib.vattn_status_string.restype = ctypes.c_char_p
     lib.vattn_last_hip_error.argtypes = []
@@ -111,6 +124,57 @@ def forward_f16_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: i
                                  mode, stream or None)
 
 
+def rope_table_raw(table_ptr: int, n_positions: int, rope_dims: int, base: float,
+                   factors=None, pos_offset: int = 0, stream: int = 0) -> int:
+    """Direct call of ``vattn_rope_table``; ``factors`` is a host sequence of
+    rope_dims/2 floats or None.  Returns the status code."""
+    fac = None
+    if factors is not None:
+        vals = [float(x) for x in factors]
+        # the library reads rope_dims/2 values from this host array
+        if len(vals) != int(rope_dims) // 2 or len(vals) == 0:
+            raise ValueError("factors must hold rope_dims/2 = %d values, got %d"
+                             % (int(rope_dims) // 2, len(vals)))
+        fac = (ctypes.c_float * len(vals))(*vals)
+    return lib.vattn_rope_table(table_ptr or None, int(n_positions), int(rope_dims),
+                                float(base),
+                                None if fac is None else ctypes.cast(fac, ctypes.c_void_p),
+                                int(pos_offset), stream or None)
+
+
+def forward_rope_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
+                     n_patches: int, head_dim: int, stride_head: int, stride_patch: int,
+                     rope_dims: int, table_ptr: int, stream: int = 0,
+                     precision: str | int = "auto", f16: bool = False) -> int:
+    """Direct call of ``vattn_forward_rope`` (or ``vattn_forward_rope_f16``);
+    returns the status code."""
+    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    fn = lib.vattn_forward_rope_f16 if f16 else lib.vattn_forward_rope
+    return fn(q_ptr or None, k_ptr or None, v_ptr or None, out_ptr or None, int(n_heads),
+              int(n_patches), int(head_dim), int(stride_head), int(stride_patch),
+              int(rope_dims), table_ptr or None, mode, stream or None)
+
+
+def rope_table(n_positions: int, rope_dims: int, base: float = 10000.0, factors=None,
+               pos_offset: int = 0, device=None,
+               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """(cos, sin) table of the NeoX rotary angles, float32
+    ``[n_positions, rope_dims // 2, 2]`` on ``device`` (default: current):
+    row n is position ``pos_offset + n``, pair i turns by
+    pos * base^(-2i/rope_dims) / factors[i].  Enqueued on ``stream``."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    table = torch.empty((int(n_positions), int(rope_dims) // 2, 2), dtype=torch.float32,
+                        device=dev)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = rope_table_raw(table.data_ptr(), n_positions, rope_dims, base, factors,
+                            pos_offset, s.cuda_stream)
+    if rc != VATTN_OK:
+        raise VattnError(rc, lib)
+    return table
+
+
 def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
                   n_patches: int, head_dim: int, stream: int = 0) -> int:
     """Direct call of the C entry point ``vattn_forward``; returns its status."""
@@ -134,15 +198,18 @@ def _check(t: torch.Tensor, name: str):
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             out: torch.Tensor | None = None, precision: str = "auto",
-            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+            stream: torch.cuda.Stream | None = None,
+            rope: torch.Tensor | None = None) -> torch.Tensor:
     """out[h] = softmax(q[h] @ k[h]^T) @ v[h] for every head (no scale inside).
 
     q, k, v, out: float32 (or all float16) [n_heads, n_patches, head_dim] on one device,
     head_dim <= 64, last dimension contiguous and the same strides for all
     four (contiguous head-major tensors, or e.g. patch-major [N, H, d]
     tensors viewed as ``x.transpose(0, 1)``).  ``out`` defaults to a new
-    tensor with q's strides.  Enqueued on ``stream`` (default: torch's
-    current stream); returns ``out`` without synchronising.
+    tensor with q's strides.  ``rope``: a table from ``rope_table`` with at
+    least n_patches rows; q and k are then rotated (patch i with row i)
+    inside the kernel.  Enqueued on ``stream`` (default: torch's current
+    stream); returns ``out`` without synchronising.
     """
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         if not isinstance(t, torch.Tensor):
@@ -168,9 +235,22 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if len(strides) != 1:
         raise ValueError("q, k, v and out must share their strides: %s" % strides)
     sh, sn = strides.pop()
+    if rope is not None:
+        if not isinstance(rope, torch.Tensor) or rope.dtype != torch.float32 or \
+                rope.dim() != 3 or rope.shape[2] != 2 or not rope.is_contiguous():
+            raise ValueError("rope must be a contiguous float32 [positions, rope_dims/2, 2] "
+                             "table from rope_table()")
+        if rope.device != q.device:
+            raise ValueError("rope table on %s, tensors on %s" % (rope.device, q.device))
+        if rope.shape[0] < n:
+            raise ValueError("rope table has %d rows for %d patches" % (rope.shape[0], n))
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream()
-        if q.dtype == torch.float16:
+        if rope is not None:
+            rc = forward_rope_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  h, n, d, sh, sn, 2 * rope.shape[1], rope.data_ptr(),
+                                  s.cuda_stream, precision, f16=q.dtype == torch.float16)
+        elif q.dtype == torch.float16:
             rc = forward_f16_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  h, n, d, sh, sn, s.cuda_stream, precision)
         elif q.is_contiguous():

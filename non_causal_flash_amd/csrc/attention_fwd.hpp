@@ -53,6 +53,16 @@
 //    matching output columns are simply not stored.  kIoVec4 moves 4- (or
 //    2-) float vectors (head_dim and strides multiples of 4), kIoScalar
 //    single floats.
+//  * Optional NeoX rotary transform of Q and K (ROPE; docs.rs page "rullama
+//    0.2.0", src/kernels/wgsl/rope_neox_backward.wgsl, the forward rotation
+//    of its header comment): pairs (x[i], x[i + half]), i < half =
+//    rope_dims/2, of the row of patch n turn by the angle whose cos/sin the
+//    table row n holds.  The rotation is applied in f32 to the Q fragment
+//    when it is loaded and to every K tile on its way into LDS, before the
+//    f16 rounding (and the hi/lo split), so rotated K never goes to HBM.  A
+//    tile thread whose columns start a pair loads both halves and the
+//    cos/sin, and stores both rotated halves; the threads of the second
+//    halves load no K.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -75,6 +85,14 @@ struct Io {
     long long stride_head;
     int stride_patch;
     int head_dim;
+};
+
+// Rotary table: row n (patch n) holds rope_dims/2 pairs (cos theta, sin
+// theta) as f32, theta = position(n) * frequency(i); half = rope_dims / 2,
+// a multiple of 4.
+struct Rope {
+    const float *cs;
+    int half;
 };
 
 // A byte offset past any buffer range: raw buffer loads there return 0.
@@ -220,11 +238,22 @@ struct TileMap {
     }
 };
 
-template <int D, int WAVES, typename T>
+template <int D, int WAVES, typename T, bool ROPE>
 struct TileRegs {
     using S = Shape<D, WAVES>;
     typename VecOf<T, S::kKWidth>::type k[S::kKVec];
     typename VecOf<T, S::kKWidth>::type v[S::kKVec];
+};
+
+// ROPE: also the second halves of the pairs whose first halves k holds, and
+// their (cos, sin) pairs, interleaved.
+template <int D, int WAVES, typename T>
+struct TileRegs<D, WAVES, T, true> {
+    using S = Shape<D, WAVES>;
+    typename VecOf<T, S::kKWidth>::type k[S::kKVec];
+    typename VecOf<T, S::kKWidth>::type v[S::kKVec];
+    typename VecOf<T, S::kKWidth>::type k2[S::kKVec];
+    float4_t cs[S::kKVec][S::kKWidth / 2];
 };
 
 // Vector of N elements at columns [col, col+N) of a row (row_off = the
@@ -233,56 +262,131 @@ struct TileRegs {
 template <typename T, int N, int IO>
 __device__ __forceinline__ typename VecOf<T, N>::type load_cols(__amdgpu_buffer_rsrc_t r,
                                                                 int row_off, int col,
-                                                                const Io &io) {
+                                                                const Io &io,
+                                                                bool enable = true) {
     constexpr int kSz = (int)sizeof(T);
     if constexpr (IO == kIoScalar) {
         typename VecOf<T, N>::type x;
 #pragma unroll
         for (int j = 0; j < N; ++j)
-            x[j] = buf_load_one<T>(r, col + j < io.head_dim ? (row_off + col + j) * kSz : kOutOfRange);
+            x[j] = buf_load_one<T>(r, enable && col + j < io.head_dim ? (row_off + col + j) * kSz
+                                                                      : kOutOfRange);
         return x;
     } else {
-        const bool in = IO == kIoDense || col < io.head_dim;
+        const bool in = enable && (IO == kIoDense || col < io.head_dim);
         return buf_load_vec<T, N>(r, in ? (row_off + col) * kSz : kOutOfRange);
     }
 }
 
-template <int D, int WAVES, int IO, typename T>
+// Buffer descriptor over table rows [row0, n_patches) of the rotary table.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rope_rsrc(const Rope &rope, int row0,
+                                                            int n_patches) {
+    const int rows = max(n_patches - row0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(rope.cs + (size_t)row0 * rope.half * 2), (short)0,
+        rows * rope.half * 8, kBufferFlags);
+}
+
+// (cos, sin) of pairs [i, i + 2*NV) of table row `row` (relative to the
+// descriptor), or zeros when !enable.
+template <int NV>
+__device__ __forceinline__ void load_cs(__amdgpu_buffer_rsrc_t r, int row, int i, int half,
+                                        bool enable, float4_t (&cs)[NV]) {
+    const int off = enable ? (row * half + i) * 8 : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        cs[j] = buf_load_vec<float, 4>(r, enable ? off + 16 * j : kOutOfRange);
+}
+
+// NeoX rotation of N columns starting a pair (x: first halves, y: second
+// halves) by the angles whose (cos, sin) cs holds, interleaved.
+template <int N>
+__device__ __forceinline__ void rotate_pairs(const typename VecOf<float, N>::type &x,
+                                             const typename VecOf<float, N>::type &y,
+                                             const float4_t (&cs)[N / 2],
+                                             typename VecOf<float, N>::type &lo,
+                                             typename VecOf<float, N>::type &hi) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const float c = cs[j / 2][2 * (j % 2)];
+        const float sn = cs[j / 2][2 * (j % 2) + 1];
+        lo[j] = x[j] * c - y[j] * sn;
+        hi[j] = x[j] * sn + y[j] * c;
+    }
+}
+
+template <int D, int WAVES, int IO, typename T, bool ROPE>
 __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
                                           int n_patches, const TileMap<D, WAVES> &m,
-                                          TileRegs<D, WAVES, T> &r, const Io &io) {
+                                          TileRegs<D, WAVES, T, ROPE> &r, const Io &io,
+                                          const Rope &rope) {
     using S = Shape<D, WAVES>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
     const int pitch = IO == kIoDense ? D : io.stride_patch;
+    // ROPE: a thread whose columns start pairs (col < half) loads both
+    // halves and the table; one whose columns are second halves loads no K.
+    bool pair = false, k_in = true;
+    __amdgpu_buffer_rsrc_t rt;
+    if constexpr (ROPE) {
+        pair = m.col < rope.half;
+        k_in = pair || m.col >= 2 * rope.half;
+        rt = rope_rsrc(rope, key0, n_patches);
+    }
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int row_off = (m.row0 + u * TileMap<D, WAVES>::kRowStep) * pitch;
-        r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io);
+        const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
+        const int row_off = row * pitch;
+        r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io, k_in);
         r.v[u] = load_cols<T, S::kKWidth, IO>(rv, row_off, m.col, io);
+        if constexpr (ROPE) {
+            r.k2[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col + rope.half, io, pair);
+            load_cs(rt, row, m.col, rope.half, pair, r.cs[u]);
+        }
     }
 }
 
 // Registers -> LDS, both row-major [key][dim] in f16 (RNE from f32); with
 // f32 inputs SPLIT also stores k_lo = f16(k - f32(f16(k))).  f16 inputs
 // are exact in f16 (no k_lo).
-template <int D, int WAVES, bool SPLIT, typename T>
-__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T> &r,
+template <int D, int WAVES, bool SPLIT, typename T, bool ROPE>
+__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
                                            _Float16 (*vh)[Lds<D>::kKRow],
-                                           const TileMap<D, WAVES> &m) {
+                                           const TileMap<D, WAVES> &m, const Rope &rope) {
     using S = Shape<D, WAVES>;
     typedef typename VecOf<float, S::kKWidth>::type Vec;
     typedef typename VecOf<_Float16, S::kKWidth>::type Half;
+    // f32 K (or rotated K) -> f16 hi, and with SPLIT lo = f16(k - f32(hi)).
+    auto put_k = [&](int row, int col, const Vec &x) __attribute__((always_inline)) {
+        const Half hi = __builtin_convertvector(x, Half);
+        *reinterpret_cast<Half *>(&kh[row][col]) = hi;
+        if constexpr (SPLIT)
+            *reinterpret_cast<Half *>(&kl[row][col]) =
+                __builtin_convertvector(x - __builtin_convertvector(hi, Vec), Half);
+    };
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
         const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
-        const Half hi = __builtin_convertvector(r.k[u], Half);
-        *reinterpret_cast<Half *>(&kh[row][m.col]) = hi;
-        if constexpr (SPLIT && sizeof(T) == 4) {
-            const Vec back = __builtin_convertvector(hi, Vec);
-            *reinterpret_cast<Half *>(&kl[row][m.col]) = __builtin_convertvector(r.k[u] - back, Half);
+        if constexpr (ROPE) {
+            // Rotated pairs, in f32 before any rounding; columns past
+            // rope_dims pass through; second-half threads store no K.
+            const Vec x = __builtin_convertvector(r.k[u], Vec);
+            const Vec y = __builtin_convertvector(r.k2[u], Vec);
+            Vec lo, hi;
+            rotate_pairs<S::kKWidth>(x, y, r.cs[u], lo, hi);
+            if (m.col < rope.half) {
+                put_k(row, m.col, lo);
+                put_k(row, m.col + rope.half, hi);
+            } else if (m.col >= 2 * rope.half) {
+                put_k(row, m.col, x);
+            }
+        } else if constexpr (sizeof(T) == 4) {
+            put_k(row, m.col, r.k[u]);
+        } else {
+            // f16 inputs are exact in f16: copied, no lo part.
+            *reinterpret_cast<Half *>(&kh[row][m.col]) = r.k[u];
         }
         *reinterpret_cast<Half *>(&vh[row][m.col]) = __builtin_convertvector(r.v[u], Half);
     }
@@ -460,15 +564,24 @@ struct IntTag {
 // hides behind a whole tile of compute.  Matrix and vector work overlap
 // across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
-template <int D, int WAVES, bool SPLIT, int IO, typename T>
-__global__ void __launch_bounds__(64 * WAVES, 4)
+// Waves per SIMD the register budget is sized for: 4 (128 VGPRs), except
+// the rotary 8-wave kernels, whose two tile loads per thread carry both pair
+// halves and the cos/sin: 2 (256 VGPRs), i.e. one workgroup per CU; they
+// are only launched on grids of at most one workgroup per CU.
+template <int WAVES, bool ROPE>
+constexpr int kMinWavesPerSimd = ROPE && WAVES == 8 ? 2 : 4;
+
+template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
+__global__ void __launch_bounds__(64 * WAVES, (kMinWavesPerSimd<WAVES, ROPE>))
 attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      const T *__restrict__ v, T *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks, float lo_window,
-                     float lo_gate, Io io) {
+                     float lo_gate, Io io, Rope rope) {
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
-    constexpr bool KLO = SPLIT && sizeof(T) == 4;  // k_lo tiles (f32 inputs only)
+    // k_lo tiles: f32 K, or rotated K (f16 inputs are exact in f16 only
+    // before the rotation).
+    constexpr bool KLO = SPLIT && (sizeof(T) == 4 || ROPE);
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
@@ -498,21 +611,42 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     half8_t ql[L::kKSteps];
     __amdgpu_buffer_rsrc_t rq;
     if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
+    typedef typename VecOf<T, 4>::type T4;
+    // Four query columns [c, c+4) of this lane's row as f32 (0 past the head).
+    auto q4 = [&](int c) __attribute__((always_inline)) {
+        float4_t x = zero4();
+        if (row < n_patches) {
+            if constexpr (IO == kIoDense)
+                x = __builtin_convertvector(*reinterpret_cast<const T4 *>(qg + row * D + c), float4_t);
+            else
+                x = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io),
+                                            float4_t);
+        }
+        return x;
+    };
+    // ROPE: columns [c, c+4) lie on one side of half and of rope_dims (both
+    // multiples of 4); rotate them with their partner columns.
+    auto q4_rotated = [&](int c) __attribute__((always_inline)) {
+        float4_t x = q4(c);
+        if constexpr (ROPE) {
+            if (c < 2 * rope.half) {
+                const bool first = c < rope.half;
+                const int i = first ? c : c - rope.half;
+                const float4_t y = q4(first ? c + rope.half : c - rope.half);
+                float4_t cs[2];
+                load_cs(rope_rsrc(rope, 0, n_patches), row, i, rope.half, true, cs);
+                float4_t lo, hi;
+                // first half: x is x[i], y is x[i + half]; else the reverse.
+                rotate_pairs<4>(first ? x : y, first ? y : x, cs, lo, hi);
+                x = first ? lo : hi;
+            }
+        }
+        return x;
+    };
 #pragma unroll
     for (int st = 0; st < L::kKSteps; ++st) {
-        float4_t x0 = zero4(), x1 = zero4();
         const int c = 32 * st + 8 * g4;
-        typedef typename VecOf<T, 4>::type T4;
-        if constexpr (IO == kIoDense) {
-            if (row < n_patches) {
-                const T *p = qg + row * D + c;
-                x0 = __builtin_convertvector(*reinterpret_cast<const T4 *>(p), float4_t);
-                x1 = __builtin_convertvector(*reinterpret_cast<const T4 *>(p + 4), float4_t);
-            }
-        } else if (row < n_patches) {
-            x0 = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io), float4_t);
-            x1 = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c + 4, io), float4_t);
-        }
+        float4_t x0 = q4_rotated(c), x1 = q4_rotated(c + 4);
         x0 *= kLog2e;
         x1 *= kLog2e;
         const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
@@ -526,10 +660,10 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         }
     }
 
-    TileRegs<D, WAVES, T> regs;
-    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
-    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map);
-    if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
+    TileRegs<D, WAVES, T, ROPE> regs;
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io, rope);
+    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope);
+    if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io, rope);
     __syncthreads();
 
     float4_t o[L::kDBlocks];
@@ -547,9 +681,9 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         // before the barrier.
         if (t + 1 < n_tiles) {
             store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
-                                           vt_s[BUF ^ 1], map);
+                                           vt_s[BUF ^ 1], map, rope);
             if (t + 2 < n_tiles)
-                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
+                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io, rope);
         }
         float4_t s[4];
         // Correction window of the SPLIT kernel: every block of the first

@@ -4,9 +4,34 @@
 #include "vattn.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "attention_fwd.hpp"
+
+namespace vattn {
+
+// Rotary table: angles pos * w[i], w[i] = base^(-2i/rope_dims) / factors[i]
+// (computed on the host in double precision).
+struct RopeFreqs {
+    double w[32];
+};
+
+// One thread per (position, pair): cos and sin of the float64 angle,
+// rounded to float32, stored as one float2 (vector store).
+__global__ void __launch_bounds__(256)
+rope_table_kernel(float *table, int n_positions, int half, int pos_offset, RopeFreqs f) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)n_positions * half) return;
+    const int n = (int)(idx / half);
+    const int i = (int)(idx - (int64_t)n * half);
+    const double theta = (double)(pos_offset + n) * f.w[i];
+    double sn, cs;
+    sincos(theta, &sn, &cs);
+    reinterpret_cast<float2_t *>(table)[idx] = (float2_t){(float)cs, (float)sn};
+}
+
+}  // namespace vattn
 
 namespace {
 
@@ -37,68 +62,92 @@ struct SplitPolicy {
     float gate;
 };
 
-template <int D, int WAVES, bool SPLIT, int IO, typename T>
-hipError_t launch(const T *q, const T *k, const T *v, T *out,
-                  int n_heads, int n_patches, SplitPolicy pol, vattn::Io io,
-                  hipStream_t stream) {
+// Everything a launch needs besides the tensor pointers.
+struct LaunchArgs {
+    int n_heads;
+    int n_patches;
+    SplitPolicy pol;
+    vattn::Io io;
+    vattn::Rope rope;
+    hipStream_t stream;
+};
+
+template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
+hipError_t launch(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     constexpr int kBlockM = vattn::Shape<D, WAVES>::kBlockM;
+    int n_patches = a.n_patches;
     int q_blocks = (n_patches + kBlockM - 1) / kBlockM;
-    int total_blocks = q_blocks * n_heads;
-    void *args[] = {(void *)&q,           (void *)&k,          (void *)&v,
-                    (void *)&out,         (void *)&n_patches,  (void *)&q_blocks,
-                    (void *)&total_blocks, (void *)&pol.window, (void *)&pol.gate,
-                    (void *)&io};
+    int total_blocks = q_blocks * a.n_heads;
+    float window = a.pol.window, gate = a.pol.gate;
+    vattn::Io io = a.io;
+    vattn::Rope rope = a.rope;
+    void *args[] = {(void *)&q,            (void *)&k,         (void *)&v,
+                    (void *)&out,          (void *)&n_patches, (void *)&q_blocks,
+                    (void *)&total_blocks, (void *)&window,    (void *)&gate,
+                    (void *)&io,           (void *)&rope};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT, IO, T>),
-        dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, stream);
+        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT, IO, T, ROPE>),
+        dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, a.stream);
 }
 
 // 16-wave workgroups (256 query rows) share each K/V tile among twice the
 // queries, halving L2 traffic and conversion work per query; they run one per
-// CU.  Use them when they still give every CU at least one workgroup.
-template <int D, bool SPLIT, int IO, typename T>
-hipError_t launch_any(const T *q, const T *k, const T *v, T *out,
-                      int n_heads, int n_patches, SplitPolicy pol, vattn::Io io,
-                      hipStream_t stream) {
+// CU.  Use them when they still give every CU at least one workgroup.  The
+// rotary 8-wave kernels fit one workgroup per CU (register budget), so the
+// rotary path switches to 16 waves as soon as 8-wave blocks would exceed the
+// CU count.
+template <int D, bool SPLIT, int IO, typename T, bool ROPE>
+hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     const int64_t wide_blocks =
-        (int64_t)n_heads * (((int64_t)n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
-                            vattn::Shape<D, 16>::kBlockM);
-    if (wide_blocks >= kCusPerDevice)
-        return launch<D, 16, SPLIT, IO, T>(q, k, v, out, n_heads, n_patches, pol, io, stream);
-    return launch<D, 8, SPLIT, IO, T>(q, k, v, out, n_heads, n_patches, pol, io, stream);
+        (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
+                              vattn::Shape<D, 16>::kBlockM);
+    if (wide_blocks >= (ROPE ? kCusPerDevice / 2 : kCusPerDevice))
+        return launch<D, 16, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+    return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
 }
 
-template <int D, int IO, typename T>
-hipError_t launch_mode(const T *q, const T *k, const T *v, T *out,
-                       int n_heads, int n_patches, bool split, SplitPolicy pol,
-                       vattn::Io io, hipStream_t stream) {
-    return split ? launch_any<D, true, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream)
-                 : launch_any<D, false, IO>(q, k, v, out, n_heads, n_patches, pol, io, stream);
+template <int D, int IO, typename T, bool ROPE>
+hipError_t launch_mode(const T *q, const T *k, const T *v, T *out, bool split,
+                       const LaunchArgs &a) {
+    return split ? launch_any<D, true, IO, T, ROPE>(q, k, v, out, a)
+                 : launch_any<D, false, IO, T, ROPE>(q, k, v, out, a);
 }
 
-template <int D, typename T>
-hipError_t launch_io(const T *q, const T *k, const T *v, T *out,
-                     int n_heads, int n_patches, bool split, SplitPolicy pol, vattn::Io io,
-                     int mode, hipStream_t stream) {
+template <int D, typename T, bool ROPE>
+hipError_t launch_io(const T *q, const T *k, const T *v, T *out, bool split, int mode,
+                     const LaunchArgs &a) {
     if (mode == vattn::kIoDense)
-        return launch_mode<D, vattn::kIoDense>(q, k, v, out, n_heads, n_patches, split, pol, io, stream);
+        return launch_mode<D, vattn::kIoDense, T, ROPE>(q, k, v, out, split, a);
     if (mode == vattn::kIoVec4)
-        return launch_mode<D, vattn::kIoVec4>(q, k, v, out, n_heads, n_patches, split, pol, io, stream);
-    return launch_mode<D, vattn::kIoScalar>(q, k, v, out, n_heads, n_patches, split, pol, io, stream);
+        return launch_mode<D, vattn::kIoVec4, T, ROPE>(q, k, v, out, split, a);
+    return launch_mode<D, vattn::kIoScalar, T, ROPE>(q, k, v, out, split, a);
 }
 
-// Checks and dispatch shared by the f32 and f16 entry points.
+template <typename T, bool ROPE>
+hipError_t launch_dim(const T *q, const T *k, const T *v, T *out, bool split, int mode,
+                      int D, const LaunchArgs &a) {
+    return D == 64 ? launch_io<64, T, ROPE>(q, k, v, out, split, mode, a)
+                   : launch_io<32, T, ROPE>(q, k, v, out, split, mode, a);
+}
+
+// Checks and dispatch shared by every attention entry point.  rope_dims = 0
+// (and no table): no rotary transform.
 template <typename T>
 int forward_impl(const T *q, const T *k, const T *v, T *out, int n_heads, int n_patches,
                  int head_dim, long long stride_head, long long stride_patch, int precision,
-                 void *stream) {
+                 int rope_dims, const float *rope_table, void *stream) {
     if (n_heads < 0 || n_patches < 0) return VATTN_ERR_SIZE;
     if (head_dim < 1 || head_dim > 64) return VATTN_ERR_HEAD_DIM;
     if (precision != VATTN_PRECISION_AUTO && precision != VATTN_PRECISION_FAST &&
         precision != VATTN_PRECISION_SPLIT)
         return VATTN_ERR_ARG;
+    const bool rope = rope_dims != 0;
+    // Rotary pairs move in 4-column vectors: half = rope_dims/2 must be a
+    // multiple of 4 so no vector straddles half or rope_dims.
+    if (rope && (rope_dims < 8 || rope_dims % 8 != 0 || rope_dims > head_dim))
+        return VATTN_ERR_ROPE;
     if (n_heads == 0 || n_patches == 0) return VATTN_OK;
-    if (!q || !k || !v || !out) return VATTN_ERR_NULL;
+    if (!q || !k || !v || !out || (rope && !rope_table)) return VATTN_ERR_NULL;
 
     // Strides: rows of head_dim elements that never overlap.  Either the
     // heads are outermost (stride_head covers a whole head) or the patches
@@ -127,12 +176,16 @@ int forward_impl(const T *q, const T *k, const T *v, T *out, int n_heads, int n_
     const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
     if (mis & (align - 1)) return VATTN_ERR_ALIGN;
+    if (rope && (reinterpret_cast<uintptr_t>(rope_table) & 15)) return VATTN_ERR_ALIGN;
 
     const uintptr_t bytes = (uintptr_t)(((H - 1) * sh + (N - 1) * sn + d) * (int64_t)sizeof(T));
     const uintptr_t po = reinterpret_cast<uintptr_t>(out);
     if (overlaps(po, bytes, reinterpret_cast<uintptr_t>(q), bytes) ||
         overlaps(po, bytes, reinterpret_cast<uintptr_t>(k), bytes) ||
         overlaps(po, bytes, reinterpret_cast<uintptr_t>(v), bytes))
+        return VATTN_ERR_ALIAS;
+    if (rope && overlaps(po, bytes, reinterpret_cast<uintptr_t>(rope_table),
+                         (uintptr_t)(N * (rope_dims / 2) * 8)))
         return VATTN_ERR_ALIAS;
 
     const bool split = precision != VATTN_PRECISION_FAST;
@@ -141,11 +194,11 @@ int forward_impl(const T *q, const T *k, const T *v, T *out, int n_heads, int n_
     // waves whose logits are large (kAutoWindow / kAutoGate).
     const SplitPolicy pol = precision == VATTN_PRECISION_SPLIT ? SplitPolicy{inf, -1.0f}
                                                                : SplitPolicy{kAutoWindow, kAutoGate};
-    const vattn::Io io{stride_head, (int)stride_patch, head_dim};
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const hipError_t err =
-        D == 64 ? launch_io<64>(q, k, v, out, n_heads, n_patches, split, pol, io, mode, s)
-                : launch_io<32>(q, k, v, out, n_heads, n_patches, split, pol, io, mode, s);
+    const LaunchArgs a{n_heads, n_patches, pol, vattn::Io{stride_head, (int)stride_patch, head_dim},
+                       vattn::Rope{rope_table, rope_dims / 2},
+                       reinterpret_cast<hipStream_t>(stream)};
+    const hipError_t err = rope ? launch_dim<T, true>(q, k, v, out, split, mode, D, a)
+                                : launch_dim<T, false>(q, k, v, out, split, mode, D, a);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return VATTN_ERR_HIP;
@@ -165,6 +218,7 @@ extern "C" const char *vattn_status_string(int status) {
         case VATTN_ERR_ALIAS: return "out overlaps q, k or v";
         case VATTN_ERR_HIP: return "HIP runtime error";
         case VATTN_ERR_ARG: return "unknown precision mode";
+        case VATTN_ERR_ROPE: return "invalid rotary parameters";
         default: return "unknown status";
     }
 }
@@ -176,7 +230,7 @@ extern "C" int vattn_forward_strided(const float *q, const float *k, const float
                                      int head_dim, long long stride_head,
                                      long long stride_patch, int precision, void *stream) {
     return forward_impl<float>(q, k, v, out, n_heads, n_patches, head_dim, stride_head,
-                               stride_patch, precision, stream);
+                               stride_patch, precision, 0, nullptr, stream);
 }
 
 extern "C" int vattn_forward_f16(const void *q, const void *k, const void *v, void *out,
@@ -186,7 +240,63 @@ extern "C" int vattn_forward_f16(const void *q, const void *k, const void *v, vo
     return forward_impl<_Float16>(static_cast<const _Float16 *>(q), static_cast<const _Float16 *>(k),
                                   static_cast<const _Float16 *>(v), static_cast<_Float16 *>(out),
                                   n_heads, n_patches, head_dim, stride_head, stride_patch,
-                                  precision, stream);
+                                  precision, 0, nullptr, stream);
+}
+
+extern "C" int vattn_forward_rope(const float *q, const float *k, const float *v, float *out,
+                                  int n_heads, int n_patches, int head_dim,
+                                  long long stride_head, long long stride_patch, int rope_dims,
+                                  const float *rope_table, int precision, void *stream) {
+    if (rope_dims == 0) return VATTN_ERR_ROPE;
+    return forward_impl<float>(q, k, v, out, n_heads, n_patches, head_dim, stride_head,
+                               stride_patch, precision, rope_dims, rope_table, stream);
+}
+
+extern "C" int vattn_forward_rope_f16(const void *q, const void *k, const void *v, void *out,
+                                      int n_heads, int n_patches, int head_dim,
+                                      long long stride_head, long long stride_patch,
+                                      int rope_dims, const float *rope_table, int precision,
+                                      void *stream) {
+    if (rope_dims == 0) return VATTN_ERR_ROPE;
+    return forward_impl<_Float16>(static_cast<const _Float16 *>(q), static_cast<const _Float16 *>(k),
+                                  static_cast<const _Float16 *>(v), static_cast<_Float16 *>(out),
+                                  n_heads, n_patches, head_dim, stride_head, stride_patch,
+                                  precision, rope_dims, rope_table, stream);
+}
+
+extern "C" int vattn_rope_table(float *table, int n_positions, int rope_dims, float base,
+                                const float *factors, int pos_offset, void *stream) {
+    if (rope_dims < 2 || rope_dims > 64 || rope_dims % 2 != 0) return VATTN_ERR_ROPE;
+    if (!(base > 0.0f) || !isfinite(base)) return VATTN_ERR_ROPE;
+    if (pos_offset < 0) return VATTN_ERR_ROPE;
+    if (n_positions < 0) return VATTN_ERR_SIZE;
+    const int half = rope_dims / 2;
+    if ((int64_t)pos_offset + n_positions - 1 > (int64_t)INT32_MAX) return VATTN_ERR_ROPE;
+    if ((int64_t)n_positions * half >= ((int64_t)1 << 31)) return VATTN_ERR_SIZE;
+    vattn::RopeFreqs f{};
+    for (int i = 0; i < half; ++i) {
+        double w = pow((double)base, -2.0 * (double)i / (double)rope_dims);
+        if (factors) {
+            const float fi = factors[i];
+            if (!(fi > 0.0f) || !isfinite(fi)) return VATTN_ERR_ROPE;
+            w /= (double)fi;
+        }
+        f.w[i] = w;
+    }
+    if (n_positions == 0) return VATTN_OK;
+    if (!table) return VATTN_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(table) & 15) return VATTN_ERR_ALIGN;
+    const int64_t total = (int64_t)n_positions * half;
+    void *args[] = {(void *)&table, (void *)&n_positions, (void *)&half, (void *)&pos_offset,
+                    (void *)&f};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&vattn::rope_table_kernel),
+                                           dim3((unsigned)((total + 255) / 256)), dim3(256), args,
+                                           0, reinterpret_cast<hipStream_t>(stream));
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return VATTN_ERR_HIP;
+    }
+    return VATTN_OK;
 }
 
 extern "C" int vattn_forward_precision(const float *q, const float *k,

@@ -43,7 +43,7 @@ def test_library_links_only_one_hip_runtime():
 
 def test_status_strings():
     lib = vattn.lib
-    for code in range(8):
+    for code in range(9):
         s = lib.vattn_status_string(code)
         assert s and s != b"unknown status"
     assert lib.vattn_status_string(99) == b"unknown status"
@@ -176,3 +176,77 @@ def test_python_wrapper_rejects_bad_tensors():
         vattn.forward(x.half(), x, x)  # mixed dtypes
     with pytest.raises(ValueError):
         vattn.forward(x, x, x.transpose(1, 2).contiguous().transpose(1, 2))  # strided last dim
+
+
+# ------------------------------------------------------------------ rotary
+T = 0x50000000  # fake 16-byte aligned table address
+
+
+@pytest.mark.parametrize("rope_dims,table,status", [
+    (0, T, vattn.VATTN_ERR_ROPE),        # the rope entry needs rotary dims
+    (4, T, vattn.VATTN_ERR_ROPE),        # below 8
+    (12, T, vattn.VATTN_ERR_ROPE),       # not a multiple of 8
+    (72, T, vattn.VATTN_ERR_ROPE),       # above head_dim
+    (64, 0, vattn.VATTN_ERR_NULL),
+    (64, T + 8, vattn.VATTN_ERR_ALIGN),
+    (64, O + 64, vattn.VATTN_ERR_ALIAS),  # out overlaps the table
+])
+def test_rope_forward_validation(rope_dims, table, status):
+    for f16 in (False, True):
+        assert vattn.forward_rope_raw(A, B, C, O, H, N, 64, N * 64, 64, rope_dims, table,
+                                      f16=f16) == status
+
+
+def test_rope_dims_above_head_dim():
+    assert vattn.forward_rope_raw(A, B, C, O, H, N, 40, N * 40, 40, 48, T) == vattn.VATTN_ERR_ROPE
+
+
+def test_rope_empty_shapes_are_no_ops():
+    assert vattn.forward_rope_raw(0, 0, 0, 0, 0, N, 64, 64, 64, 64, 0) == vattn.VATTN_OK
+    # invalid rotary dims are reported even when there is nothing to do
+    assert vattn.forward_rope_raw(0, 0, 0, 0, 0, N, 64, 64, 64, 6, 0) == vattn.VATTN_ERR_ROPE
+
+
+def test_rope_forward_reaches_launch():
+    if torch.cuda.is_available():
+        pytest.skip("launch would run on the GPU")
+    assert vattn.forward_rope_raw(A, B, C, O, H, N, 64, N * 64, 64, 32, T) == vattn.VATTN_ERR_HIP
+
+
+@pytest.mark.parametrize("args,status", [
+    ((T, 10, 0, 10000.0), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 7, 10000.0), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 66, 10000.0), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 8, 0.0), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 8, -5.0), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 8, float("inf")), vattn.VATTN_ERR_ROPE),
+    ((T, 10, 8, float("nan")), vattn.VATTN_ERR_ROPE),
+    ((T, -1, 8, 10000.0), vattn.VATTN_ERR_SIZE),
+    ((0, 10, 8, 10000.0), vattn.VATTN_ERR_NULL),
+    ((T + 4, 10, 8, 10000.0), vattn.VATTN_ERR_ALIGN),
+    ((0, 0, 8, 10000.0), vattn.VATTN_OK),
+])
+def test_rope_table_validation(args, status):
+    assert vattn.rope_table_raw(*args) == status
+
+
+def test_rope_table_factors_and_positions():
+    assert vattn.rope_table_raw(T, 10, 8, 100.0, [1.0, 2.0, 0.0, 1.0]) == vattn.VATTN_ERR_ROPE
+    assert vattn.rope_table_raw(T, 10, 8, 100.0, [1.0, float("nan"), 1.0, 1.0]) == \
+        vattn.VATTN_ERR_ROPE
+    assert vattn.rope_table_raw(T, 10, 8, 100.0, None, -1) == vattn.VATTN_ERR_ROPE
+    assert vattn.rope_table_raw(T, 10, 8, 100.0, None, 2**31 - 5) == vattn.VATTN_ERR_ROPE
+    with pytest.raises(ValueError):
+        vattn.rope_table_raw(T, 10, 8, 100.0, [1.0, 2.0])  # host array too short
+
+
+def test_rope_table_reaches_launch():
+    if torch.cuda.is_available():
+        pytest.skip("launch would run on the GPU")
+    assert vattn.rope_table_raw(T, 10, 8, 100.0, [1.0, 2.0, 3.0, 4.0], 7) == vattn.VATTN_ERR_HIP
+
+
+def test_python_wrapper_rejects_bad_rope_table():
+    x = torch.zeros(2, 8, 64)
+    with pytest.raises(ValueError):
+        vattn.forward(x, x, x, rope=torch.zeros(8, 32, 2))  # CPU tensors are rejected first

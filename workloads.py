@@ -25,12 +25,15 @@ id    H       N       d         distribution
 7     16      1024    40        Q ~ N(0,1)/sqrt(40), K, V ~ N(0,1) (head_dim 40)
 8     16      1024    64        as 3, stored as f16
 9     128     4096    64        as 5, stored as f16
+10    16      1024    64        as 3, Q and K rotated (NeoX, rope_dims 64, base 1e4)
+11    128     4096    64        as 5, Q and K rotated (NeoX, rope_dims 64, base 1e4)
 ====  ======  ======  ========  ===================================================
 
 Workloads 1-5 are the head-major f32 [H][N][d] cases; 6 and 7 exercise the
 strided (patch-major) access and a head_dim that is neither 32 nor 64; 8
 and 9 the f16 tensors (the f32 draws rounded to f16, round-to-nearest-even;
-both sides then see the same f16 values).
+both sides then see the same f16 values); 10 and 11 the rotary transform of
+Q and K, patch n at position n (the drawn arrays are the unrotated inputs).
 ``make_inputs`` always returns head-major arrays; ``to_layout`` gives the
 storage order a workload is run in.
 
@@ -53,6 +56,8 @@ class Workload:
     kind: str  # "normal" or "sharp"
     layout: str = "head"  # "head": [H][N][d]; "patch": [N][H][d]
     dtype: str = "f32"    # element type in HBM: "f32" or "f16"
+    rope_dims: int = 0    # rotary dimensions of Q and K (0: none)
+    rope_base: float = 10000.0
 
     @property
     def shape(self):
@@ -85,6 +90,8 @@ WORKLOADS = {
     7: Workload(7, "vit_h16_n1024_d40", 16, 1024, 40, "normal"),
     8: Workload(8, "vit_f16_h16_n1024_d64", 16, 1024, 64, "normal", dtype="f16"),
     9: Workload(9, "vit_f16_sharp_h128_n4096_d64", 128, 4096, 64, "sharp", dtype="f16"),
+    10: Workload(10, "vit_rope_h16_n1024_d64", 16, 1024, 64, "normal", rope_dims=64),
+    11: Workload(11, "vit_rope_sharp_h128_n4096_d64", 128, 4096, 64, "sharp", rope_dims=64),
 }
 
 
