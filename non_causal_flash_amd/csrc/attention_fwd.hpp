@@ -120,7 +120,7 @@ struct Lds {
 // How the threads of a WAVES-wave workgroup share one K/V tile.
 template <int D, int WAVES>
 struct Shape {
-    static_assert(WAVES == 8 || WAVES == 16, "8 or 16 waves per workgroup");
+    static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "4, 8 or 16 waves per workgroup");
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kBlockM = kRowsPerWave * WAVES;      // query rows per workgroup
     static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) elements per thread
@@ -422,7 +422,8 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
             s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
         }
     }
-    if constexpr (SPLIT) {
+    // lo_window is wave-uniform: skip the block tests when no block can pass.
+    if (SPLIT && lo_window != -__builtin_inff()) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const float lane_max = fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3]));
@@ -557,22 +558,21 @@ struct IntTag {
     static constexpr int value = V;
 };
 
+// Waves per SIMD the register budget is sized for: 4 (128 VGPRs) for the
+// 8- and 16-wave workgroups; the 4-wave workgroups of small grids (one wave
+// per SIMD each, four tile loads per thread) get 2 (256 VGPRs).
+template <int WAVES>
+constexpr int kMinWavesPerSimd = WAVES == 4 ? 2 : 4;
+
 // ------------------------------------------------------------------ kernel
 // Per key tile t (one barrier each): tile t+1, already in registers, is
 // converted into LDS buffer (t+1)%2 and the loads of tile t+2 are issued;
 // then QK(t) from buffer t%2, softmax and PV(t).  A tile's HBM/L2 latency
 // hides behind a whole tile of compute.  Matrix and vector work overlap
-// across the 4 waves each SIMD holds.  The loop is unrolled by two so LDS
+// across the waves each SIMD holds.  The loop is unrolled by two so LDS
 // buffer addresses are immediates.
-// Waves per SIMD the register budget is sized for: 4 (128 VGPRs), except
-// the rotary 8-wave kernels, whose two tile loads per thread carry both pair
-// halves and the cos/sin: 2 (256 VGPRs), i.e. one workgroup per CU; they
-// are only launched on grids of at most one workgroup per CU.
-template <int WAVES, bool ROPE>
-constexpr int kMinWavesPerSimd = ROPE && WAVES == 8 ? 2 : 4;
-
 template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
-__global__ void __launch_bounds__(64 * WAVES, (kMinWavesPerSimd<WAVES, ROPE>))
+__global__ void __launch_bounds__(64 * WAVES, kMinWavesPerSimd<WAVES>)
 attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      const T *__restrict__ v, T *__restrict__ out,
                      int n_patches, int q_blocks, int total_blocks, float lo_window,

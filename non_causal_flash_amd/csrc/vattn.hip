@@ -90,12 +90,13 @@ hipError_t launch(const T *q, const T *k, const T *v, T *out, const LaunchArgs &
         dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, a.stream);
 }
 
-// 16-wave workgroups (256 query rows) share each K/V tile among twice the
-// queries, halving L2 traffic and conversion work per query; they run one per
-// CU.  Use them when they still give every CU at least one workgroup.  The
-// rotary 8-wave kernels fit one workgroup per CU (register budget), so the
-// rotary path switches to 16 waves as soon as 8-wave blocks would exceed the
-// CU count.
+// Workgroup size.  16 waves (256 query rows) share each K/V tile among the
+// most queries (least L2 traffic and conversion work per query) and run one
+// per CU: used when they still give every CU a workgroup.  Smaller grids
+// take 8 waves (two workgroups per CU) while those fill the CUs, and 4 waves
+// (64 rows) below that, so that every CU gets work.  The rotary kernels
+// hold more tile registers per thread and skip the 8-wave step: their
+// 8-wave shape would need two workgroups per CU at 128 VGPRs.
 template <int D, bool SPLIT, int IO, typename T, bool ROPE>
 hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     const int64_t wide_blocks =
@@ -103,7 +104,11 @@ hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchAr
                               vattn::Shape<D, 16>::kBlockM);
     if (wide_blocks >= (ROPE ? kCusPerDevice / 2 : kCusPerDevice))
         return launch<D, 16, SPLIT, IO, T, ROPE>(q, k, v, out, a);
-    return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+    if constexpr (!ROPE) {
+        if (2 * wide_blocks >= kCusPerDevice)
+            return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+    }
+    return launch<D, 4, SPLIT, IO, T, ROPE>(q, k, v, out, a);
 }
 
 template <int D, int IO, typename T, bool ROPE>

@@ -159,3 +159,25 @@ def test_strided_c_abi_direct(vattn):
     assert np.all(np.isnan(host[:, h * d:]))
     got = host[:, :h * d].reshape(n, h, d).transpose(1, 0, 2)
     _assert_close(got, oracle.attention_f64(q, k, v), "strided c-abi")
+
+
+# Grids that select each workgroup shape: 16-wave blocks (256 rows) when
+# there are at least 256 of them, 8-wave blocks while 2x that reaches 256,
+# 4-wave blocks (64 rows) below.
+WORKGROUP_SHAPES = [("4 waves", 2, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000)]
+
+
+@pytest.mark.parametrize("label,h,n", WORKGROUP_SHAPES, ids=[s[0] for s in WORKGROUP_SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_every_workgroup_shape(vattn, label, h, n, dtype):
+    q, k, v = workloads.make_custom(h, n, 64, "sharp", seed=h + n)
+    if dtype == "f16":
+        q, k, v = (x.astype(np.float16) for x in (q, k, v))
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    rows = workloads.sample_rows(h, n, per_head=12)
+    ref = oracle.attention_rows_f64(q, k, v, rows)
+    for precision in ("auto", "split"):
+        out = vattn.forward(dq, dk, dv, precision=precision)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().reshape(-1, 64)[rows]
+        _assert_close(got, ref, "%s %s %s" % (label, dtype, precision))
