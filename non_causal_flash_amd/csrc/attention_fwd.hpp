@@ -59,10 +59,12 @@
 //    rope_dims/2, of the row of patch n turn by the angle whose cos/sin the
 //    table row n holds.  The rotation is applied in f32 to the Q fragment
 //    when it is loaded and to every K tile on its way into LDS, before the
-//    f16 rounding (and the hi/lo split), so rotated K never goes to HBM.  A
-//    tile thread whose columns start a pair loads both halves and the
-//    cos/sin, and stores both rotated halves; the threads of the second
-//    halves load no K.
+//    f16 rounding (and the hi/lo split), so rotated K never goes to HBM.
+//    A tile thread holds the columns it loaded; the other half of each pair
+//    sits in a lane of the same row (half/width lanes away) and is fetched
+//    with ds_bpermute.  The tile's cos/sin rows (one contiguous slice of the
+//    table) are copied global -> LDS by buffer loads with an LDS
+//    destination, one tile ahead like K and V, so they take no registers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -245,16 +247,7 @@ struct TileRegs {
     typename VecOf<T, S::kKWidth>::type v[S::kKVec];
 };
 
-// ROPE: also the second halves of the pairs whose first halves k holds, and
-// their (cos, sin) pairs, interleaved.
-template <int D, int WAVES, typename T>
-struct TileRegs<D, WAVES, T, true> {
-    using S = Shape<D, WAVES>;
-    typename VecOf<T, S::kKWidth>::type k[S::kKVec];
-    typename VecOf<T, S::kKWidth>::type v[S::kKVec];
-    typename VecOf<T, S::kKWidth>::type k2[S::kKVec];
-    float4_t cs[S::kKVec][S::kKWidth / 2];
-};
+
 
 // Vector of N elements at columns [col, col+N) of a row (row_off = the
 // row's element offset): the strided modes move columns >= head_dim out of
@@ -287,62 +280,75 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rope_rsrc(const Rope &rope, in
         rows * rope.half * 8, kBufferFlags);
 }
 
-// (cos, sin) of pairs [i, i + 2*NV) of table row `row` (relative to the
-// descriptor), or zeros when !enable.
-template <int NV>
-__device__ __forceinline__ void load_cs(__amdgpu_buffer_rsrc_t r, int row, int i, int half,
-                                        bool enable, float4_t (&cs)[NV]) {
-    const int off = enable ? (row * half + i) * 8 : kOutOfRange;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        cs[j] = buf_load_vec<float, 4>(r, enable ? off + 16 * j : kOutOfRange);
+// (cos, sin) of pairs [i, i + 4) of table row `row` (relative to the
+// descriptor), interleaved.
+__device__ __forceinline__ void load_cs4(__amdgpu_buffer_rsrc_t r, int row, int i, int half,
+                                         float4_t (&cs)[2]) {
+    const int off = (row * half + i) * 8;
+    cs[0] = buf_load_vec<float, 4>(r, off);
+    cs[1] = buf_load_vec<float, 4>(r, off + 16);
 }
 
-// NeoX rotation of N columns starting a pair (x: first halves, y: second
-// halves) by the angles whose (cos, sin) cs holds, interleaved.
-template <int N>
-__device__ __forceinline__ void rotate_pairs(const typename VecOf<float, N>::type &x,
-                                             const typename VecOf<float, N>::type &y,
-                                             const float4_t (&cs)[N / 2],
-                                             typename VecOf<float, N>::type &lo,
-                                             typename VecOf<float, N>::type &hi) {
+// LDS copy of the cos/sin rows of one key tile: kTileN rows of half
+// (cos, sin) pairs, as in the table.
+template <int D>
+struct CsTile {
+    static constexpr int kFloats = kTileN * (D / 2) * 2;
+};
+
+// Issue the copy of the table rows [key0, key0 + kTileN) into `dst` (LDS):
+// 1 KB per wave instruction (64 lanes x 16 bytes, lane l at byte 16 l), the
+// slice's 512*half bytes split over the waves.  Rows past n_patches read 0.
+template <int WAVES>
+__device__ __forceinline__ void copy_cs_tile(const Rope &rope, int key0, int n_patches,
+                                             float *dst, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t r = rope_rsrc(rope, key0, n_patches);
+    const int chunks = rope.half / 2;  // 1 KB chunks
+    // The LDS destination (M0) must be wave-uniform.
+    for (int c = __builtin_amdgcn_readfirstlane(wave); c < chunks; c += WAVES)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(dst + 256 * c), 16, 1024 * c + 16 * lane,
+            0, 0, 0);
+}
+
+// The tile loads of a step have landed (registers and LDS copies): all
+// vector-memory counters of this wave drained.  Before a barrier this makes
+// the LDS copies of every wave visible to every wave.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// NeoX rotation of 4 columns of one side of the pairs: x holds this side, y
+// the other side of the same pairs, cs their (cos, sin) interleaved.  First
+// halves: x c - y s; second halves: y s + x c.
+__device__ __forceinline__ float4_t rotate4(const float4_t &x, const float4_t &y,
+                                            const float4_t (&cs)[2], bool first) {
+    float4_t r;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
+    for (int j = 0; j < 4; ++j) {
         const float c = cs[j / 2][2 * (j % 2)];
-        const float sn = cs[j / 2][2 * (j % 2) + 1];
-        lo[j] = x[j] * c - y[j] * sn;
-        hi[j] = x[j] * sn + y[j] * c;
+        const float sn = first ? -cs[j / 2][2 * (j % 2) + 1] : cs[j / 2][2 * (j % 2) + 1];
+        r[j] = x[j] * c + y[j] * sn;
     }
+    return r;
+}
+
+// Value of `x` in lane `src` of the wave (ds_bpermute, all lanes active).
+__device__ __forceinline__ float lane_fetch(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
 template <int D, int WAVES, int IO, typename T, bool ROPE>
 __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
                                           int n_patches, const TileMap<D, WAVES> &m,
-                                          TileRegs<D, WAVES, T, ROPE> &r, const Io &io,
-                                          const Rope &rope) {
+                                          TileRegs<D, WAVES, T, ROPE> &r, const Io &io) {
     using S = Shape<D, WAVES>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
     const int pitch = IO == kIoDense ? D : io.stride_patch;
-    // ROPE: a thread whose columns start pairs (col < half) loads both
-    // halves and the table; one whose columns are second halves loads no K.
-    bool pair = false, k_in = true;
-    __amdgpu_buffer_rsrc_t rt;
-    if constexpr (ROPE) {
-        pair = m.col < rope.half;
-        k_in = pair || m.col >= 2 * rope.half;
-        rt = rope_rsrc(rope, key0, n_patches);
-    }
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
-        const int row_off = row * pitch;
-        r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io, k_in);
+        const int row_off = (m.row0 + u * TileMap<D, WAVES>::kRowStep) * pitch;
+        r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io);
         r.v[u] = load_cols<T, S::kKWidth, IO>(rv, row_off, m.col, io);
-        if constexpr (ROPE) {
-            r.k2[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col + rope.half, io, pair);
-            load_cs(rt, row, m.col, rope.half, pair, r.cs[u]);
-        }
     }
 }
 
@@ -354,7 +360,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
                                            _Float16 (*vh)[Lds<D>::kKRow],
-                                           const TileMap<D, WAVES> &m, const Rope &rope) {
+                                           const TileMap<D, WAVES> &m, const Rope &rope,
+                                           const float *cs_lds, int lane) {
     using S = Shape<D, WAVES>;
     typedef typename VecOf<float, S::kKWidth>::type Vec;
     typedef typename VecOf<_Float16, S::kKWidth>::type Half;
@@ -366,22 +373,42 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE> &r,
             *reinterpret_cast<Half *>(&kl[row][col]) =
                 __builtin_convertvector(x - __builtin_convertvector(hi, Vec), Half);
     };
+    // ROPE: this lane's columns [col, col + width) are first halves
+    // (col < half), second halves (col < 2 half) or unrotated; the other
+    // half of its pairs is in the lane half/width away in the same row.
+    bool first = false, rotated = false;
+    int partner = lane, pair_i = 0;
+    if constexpr (ROPE) {
+        first = m.col < rope.half;
+        rotated = m.col < 2 * rope.half;
+        const int shift = rope.half / S::kKWidth;
+        partner = first ? lane + shift : (rotated ? lane - shift : lane);
+        pair_i = first ? m.col : m.col - rope.half;
+    }
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
         const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
         if constexpr (ROPE) {
-            // Rotated pairs, in f32 before any rounding; columns past
-            // rope_dims pass through; second-half threads store no K.
             const Vec x = __builtin_convertvector(r.k[u], Vec);
-            const Vec y = __builtin_convertvector(r.k2[u], Vec);
-            Vec lo, hi;
-            rotate_pairs<S::kKWidth>(x, y, r.cs[u], lo, hi);
-            if (m.col < rope.half) {
-                put_k(row, m.col, lo);
-                put_k(row, m.col + rope.half, hi);
-            } else if (m.col >= 2 * rope.half) {
-                put_k(row, m.col, x);
+            Vec y, k_rot;
+#pragma unroll
+            for (int j = 0; j < S::kKWidth; ++j) y[j] = lane_fetch(x[j], partner);
+            if (rotated) {
+                const float *c = cs_lds + 2 * (row * rope.half + pair_i);
+                if constexpr (S::kKWidth == 4) {
+                    const float4_t cs[2] = {*reinterpret_cast<const float4_t *>(c),
+                                            *reinterpret_cast<const float4_t *>(c + 4)};
+                    k_rot = rotate4(x, y, cs, first);
+                } else {
+                    const float4_t cs[2] = {*reinterpret_cast<const float4_t *>(c), zero4()};
+                    const float4_t rr = rotate4((float4_t){x[0], x[1], 0.f, 0.f},
+                                                (float4_t){y[0], y[1], 0.f, 0.f}, cs, first);
+                    k_rot = (Vec){rr[0], rr[1]};
+                }
+            } else {
+                k_rot = x;
             }
+            put_k(row, m.col, k_rot);
         } else if constexpr (sizeof(T) == 4) {
             put_k(row, m.col, r.k[u]);
         } else {
@@ -586,6 +613,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
     _Float16 kl_s[KLO ? 2 : 1][KLO ? kTileN : 1][L::kKRow];
+    __shared__ __attribute__((aligned(16))) float cs_s[ROPE ? 2 : 1][ROPE ? CsTile<D>::kFloats : 4];
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
@@ -634,11 +662,8 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 const int i = first ? c : c - rope.half;
                 const float4_t y = q4(first ? c + rope.half : c - rope.half);
                 float4_t cs[2];
-                load_cs(rope_rsrc(rope, 0, n_patches), row, i, rope.half, true, cs);
-                float4_t lo, hi;
-                // first half: x is x[i], y is x[i + half]; else the reverse.
-                rotate_pairs<4>(first ? x : y, first ? y : x, cs, lo, hi);
-                x = first ? lo : hi;
+                load_cs4(rope_rsrc(rope, 0, n_patches), row, i, rope.half, cs);
+                x = rotate4(x, y, cs, first);
             }
         }
         return x;
@@ -661,9 +686,25 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     }
 
     TileRegs<D, WAVES, T, ROPE> regs;
-    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io, rope);
-    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope);
-    if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io, rope);
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
+    if constexpr (ROPE) {
+        // Zero both cos/sin buffers first, so no lane ever reads LDS the
+        // copies leave unwritten; then copy tile 0's rows.
+        for (int i = tid; i < 2 * CsTile<D>::kFloats / 4; i += 64 * WAVES)
+            reinterpret_cast<float4_t *>(&cs_s[0][0])[i] = zero4();
+        __syncthreads();
+        copy_cs_tile<WAVES>(rope, 0, n_patches, cs_s[0], wave, lane);
+        wait_vmem();
+        __syncthreads();
+    }
+    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
+    if (n_tiles > 1) {
+        load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
+        if constexpr (ROPE) {
+            copy_cs_tile<WAVES>(rope, kTileN, n_patches, cs_s[1], wave, lane);
+            wait_vmem();
+        }
+    }
     __syncthreads();
 
     float4_t o[L::kDBlocks];
@@ -681,9 +722,14 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         // before the barrier.
         if (t + 1 < n_tiles) {
             store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
-                                           vt_s[BUF ^ 1], map, rope);
-            if (t + 2 < n_tiles)
-                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io, rope);
+                                           vt_s[BUF ^ 1], map, rope, cs_s[ROPE ? (BUF ^ 1) : 0],
+                                           lane);
+            if (t + 2 < n_tiles) {
+                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
+                // cos/sin of tile t+2 into the buffer tile t's store read.
+                if constexpr (ROPE)
+                    copy_cs_tile<WAVES>(rope, (t + 2) * kTileN, n_patches, cs_s[BUF], wave, lane);
+            }
         }
         float4_t s[4];
         // Correction window of the SPLIT kernel: every block of the first
@@ -700,6 +746,9 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
             softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
         else
             softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+        // ROPE: this wave's cos/sin copies must have landed before the
+        // barrier that hands them to every wave.
+        if constexpr (ROPE) wait_vmem();
         __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {
