@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 
 One step is one ``vattn_forward`` over the whole workload (every head, every
-query row) on inputs already resident in HBM.  Prints one JSON line with the
+query row) on inputs already resident in HBM; the timed steps run as one
+captured HIP graph (``--no-graph``: plain launches).  Prints one JSON line with the
 attention throughput 4*H*N^2*d / time, the roofline of the kernel against
 the dense f16 matrix-core peak, and the float64 CPU oracle timed on a bounded
 sample of the same workload on the host's cores.
@@ -96,6 +97,8 @@ def main():
     ap.add_argument("--precision", default="auto", choices=["auto", "fast", "split"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 disables it)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="time plain launches instead of one captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -123,15 +126,38 @@ def main():
     stream = torch.cuda.current_stream()
     table = vattn.rope_table(w.n_patches, w.rope_dims, w.rope_base) if w.rope_dims else None
 
-    for _ in range(args.warmup):
+    def step():
         vattn.forward(dq, dk, dv, out=out, precision=args.precision, rope=table)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
+
+    # The timed steps are issued as one HIP graph of `steps` kernel launches
+    # (captured once, replayed once), so that launches of 10-30 us are not
+    # paced by the Python call path; --no-graph times plain launches.
+    graph, launch = None, "eager launches"
+    if args.graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    step()
+            graph.replay()  # untimed first replay
+            torch.cuda.synchronize()
+            launch = "one HIP graph of %d launches" % args.steps
+        except RuntimeError as e:  # fall back to plain launches, and say so
+            graph, launch = None, "eager launches (graph capture failed: %s)" % str(e)[:80]
+            torch.cuda.synchronize()
 
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
-        vattn.forward(dq, dk, dv, out=out, precision=args.precision, rope=table)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -171,7 +197,8 @@ def main():
                    "head_dim": w.head_dim, "precision": args.precision,
                    "rope": ("NeoX rope_dims %d base %g, table built once" % (w.rope_dims, w.rope_base))
                            if w.rope_dims else None,
-                   "io": "%s %s resident in HBM" % (w.dtype, "[N][H][d]" if w.layout == "patch" else "[H][N][d]")},
+                   "io": "%s %s resident in HBM" % (w.dtype, "[N][H][d]" if w.layout == "patch" else "[H][N][d]"),
+                   "launch": launch},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),

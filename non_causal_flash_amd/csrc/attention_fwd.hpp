@@ -119,13 +119,13 @@ struct Lds {
     static constexpr int kDBlocks = D / 16;          // 16-row blocks of O^T
 };
 
-// How the threads of a WAVES-wave workgroup share one K/V tile.
-template <int D, int WAVES>
+// How the threads of a WAVES-wave workgroup share one K/V tile of TN keys.
+template <int D, int WAVES, int TN = kTileN>
 struct Shape {
     static_assert(WAVES == 4 || WAVES == 8 || WAVES == 16, "4, 8 or 16 waves per workgroup");
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kBlockM = kRowsPerWave * WAVES;      // query rows per workgroup
-    static constexpr int kTileElems = kTileN * D / kThreads;  // K (and V) elements per thread
+    static constexpr int kTileElems = TN * D / kThreads;      // K (and V) elements per thread
     static constexpr int kKWidth = kTileElems < 4 ? kTileElems : 4;  // elements per load
     static constexpr int kKVec = kTileElems / kKWidth;        // loads per thread per tensor
     static_assert(kKWidth == 2 || kKWidth == 4, "tile/thread shape");
@@ -228,9 +228,9 @@ __device__ __forceinline__ T buf_load_one(__amdgpu_buffer_rsrc_t r, int byte_off
 // the thread covers f = tid + kThreads*u of the tile in units of kKWidth
 // elements, row f / (D/kKWidth), columns kKWidth*(f % ..), so a wave reads
 // whole rows.  K and V share the mapping.
-template <int D, int WAVES>
+template <int D, int WAVES, int TN = kTileN>
 struct TileMap {
-    using S = Shape<D, WAVES>;
+    using S = Shape<D, WAVES, TN>;
     static constexpr int kPerRow = D / S::kKWidth;           // loads per row
     static constexpr int kRowStep = S::kThreads / kPerRow;   // rows between u and u+1
     int row0, col;
@@ -240,9 +240,9 @@ struct TileMap {
     }
 };
 
-template <int D, int WAVES, typename T, bool ROPE>
+template <int D, int WAVES, typename T, bool ROPE, int TN = kTileN>
 struct TileRegs {
-    using S = Shape<D, WAVES>;
+    using S = Shape<D, WAVES, TN>;
     typename VecOf<T, S::kKWidth>::type k[S::kKVec];
     typename VecOf<T, S::kKWidth>::type v[S::kKVec];
 };
@@ -336,17 +336,17 @@ __device__ __forceinline__ float lane_fetch(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-template <int D, int WAVES, int IO, typename T, bool ROPE>
+template <int D, int WAVES, int IO, typename T, bool ROPE, int TN>
 __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
-                                          int n_patches, const TileMap<D, WAVES> &m,
-                                          TileRegs<D, WAVES, T, ROPE> &r, const Io &io) {
-    using S = Shape<D, WAVES>;
+                                          int n_patches, const TileMap<D, WAVES, TN> &m,
+                                          TileRegs<D, WAVES, T, ROPE, TN> &r, const Io &io) {
+    using S = Shape<D, WAVES, TN>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
     const int pitch = IO == kIoDense ? D : io.stride_patch;
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int row_off = (m.row0 + u * TileMap<D, WAVES>::kRowStep) * pitch;
+        const int row_off = (m.row0 + u * TileMap<D, WAVES, TN>::kRowStep) * pitch;
         r.k[u] = load_cols<T, S::kKWidth, IO>(rk, row_off, m.col, io);
         r.v[u] = load_cols<T, S::kKWidth, IO>(rv, row_off, m.col, io);
     }
@@ -355,14 +355,14 @@ __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
 // Registers -> LDS, both row-major [key][dim] in f16 (RNE from f32); with
 // f32 inputs SPLIT also stores k_lo = f16(k - f32(f16(k))).  f16 inputs
 // are exact in f16 (no k_lo).
-template <int D, int WAVES, bool SPLIT, typename T, bool ROPE>
-__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE> &r,
+template <int D, int WAVES, bool SPLIT, typename T, bool ROPE, int TN>
+__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE, TN> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
                                            _Float16 (*vh)[Lds<D>::kKRow],
-                                           const TileMap<D, WAVES> &m, const Rope &rope,
+                                           const TileMap<D, WAVES, TN> &m, const Rope &rope,
                                            const float *cs_lds, int lane) {
-    using S = Shape<D, WAVES>;
+    using S = Shape<D, WAVES, TN>;
     typedef typename VecOf<float, S::kKWidth>::type Vec;
     typedef typename VecOf<_Float16, S::kKWidth>::type Half;
     // f32 K (or rotated K) -> f16 hi, and with SPLIT lo = f16(k - f32(hi)).
@@ -387,7 +387,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE> &r,
     }
 #pragma unroll
     for (int u = 0; u < S::kKVec; ++u) {
-        const int row = m.row0 + u * TileMap<D, WAVES>::kRowStep;
+        const int row = m.row0 + u * TileMap<D, WAVES, TN>::kRowStep;
         if constexpr (ROPE) {
             const Vec x = __builtin_convertvector(r.k[u], Vec);
             Vec y, k_rot;
@@ -434,14 +434,14 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // running max has weight below 2^-lo_window, so the ~2^-11 relative error
 // its q_hi.k_hi logit carries is negligible in the output.  KLO = false
 // (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
-template <int D, bool SPLIT, bool KLO>
+template <int D, bool SPLIT, bool KLO, int KB = 4>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
                                         const half8_t (&qh)[Lds<D>::kKSteps],
                                         const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
-                                        float4_t (&s)[4], int l16, int g4, float lo_window) {
+                                        float4_t (&s)[KB], int l16, int g4, float lo_window) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int st = 0; st < Lds<D>::kKSteps; ++st) {
             const half8_t a = *reinterpret_cast<const half8_t *>(
@@ -452,7 +452,7 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
     // lo_window is wave-uniform: skip the block tests when no block can pass.
     if (SPLIT && lo_window != -__builtin_inff()) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const float lane_max = fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3]));
             if (__ballot(lane_max > -lo_window)) {
 #pragma unroll
@@ -486,16 +486,16 @@ __device__ __forceinline__ half4_t read_tr16(const _Float16 *p) {
 // 4*(s%4)..+3 of the block, which yields, for lane 16g+j, dim j of keys
 // {4g..4g+3} and {16+4g..16+4g+3}: the keys the P operand of that lane
 // holds, in the same order.
-template <int D>
+template <int D, int KB = 4>
 __device__ __forceinline__ void pv_tile(const _Float16 (*vh)[Lds<D>::kKRow],
-                                        const half8_t (&p)[2],
+                                        const half8_t (&p)[KB / 2],
                                         float4_t (&o)[Lds<D>::kDBlocks], int l16, int g4) {
     const int key = 4 * g4 + (l16 >> 2);
     const int dim = 4 * (l16 & 3);
 #pragma unroll
     for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KB / 2; ++ks) {
             const half4_t a0 = read_tr16(&vh[32 * ks + key][16 * db + dim]);
             const half4_t a1 = read_tr16(&vh[32 * ks + 16 + key][16 * db + dim]);
             const half8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
@@ -510,11 +510,13 @@ __device__ __forceinline__ float max4(float4_t x) {
 
 // P = 2^s as f16 MFMA operands (the key order of the S accumulator, matched
 // by vt_pos); l += the f16-rounded P.
-__device__ __forceinline__ void exp_tile(const float4_t (&s)[4], float &l_run, half8_t (&p)[2]) {
+template <int KB = 4>
+__device__ __forceinline__ void exp_tile(const float4_t (&s)[KB], float &l_run,
+                                         half8_t (&p)[KB / 2]) {
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     float lsum = l_run;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KB / 2; ++ks) {
         half2_t h[4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -537,30 +539,28 @@ __device__ __forceinline__ void exp_tile(const float4_t (&s)[4], float &l_run, h
 // wave-uniform and rare once the max settles; it carries its own copy of
 // the exponentials and the P.V product, so the common path joins the rare
 // one only after values both sides compute afresh (no register copies).
-template <int D, bool MASK>
-__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, float &m_run,
+template <int D, bool MASK, int KB = 4>
+__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0, float &m_run,
                                                 float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
                                                 const _Float16 (*vt)[Lds<D>::kKRow],
                                                 int key_lim, int l16, int g4) {
     if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
     }
+    // In-lane max over the KB x 4 scores, as a chain of 3-input maxima.
     float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-    mx = fmaxf(fmaxf(mx, s[0][3]), s[1][0]);
-    mx = fmaxf(fmaxf(mx, s[1][1]), s[1][2]);
-    mx = fmaxf(fmaxf(mx, s[1][3]), s[2][0]);
-    mx = fmaxf(fmaxf(mx, s[2][1]), s[2][2]);
-    mx = fmaxf(fmaxf(mx, s[2][3]), s[3][0]);
-    mx = fmaxf(fmaxf(mx, s[3][1]), s[3][2]);
-    mx = fmaxf(mx, s[3][3]);
+#pragma unroll
+    for (int e = 3; e + 1 < 4 * KB; e += 2)
+        mx = fmaxf(fmaxf(mx, s[e / 4][e % 4]), s[(e + 1) / 4][(e + 1) % 4]);
+    mx = fmaxf(mx, s[KB - 1][3]);
     const float m_ref = -c0[0];
     const float tile_max = max_lane_groups(mx) + m_ref;
     const bool raise = tile_max > m_run + kRescaleSlack;
-    half8_t p[2];
+    half8_t p[KB / 2];
     if (__ballot(raise)) {
         const float m_new = raise ? tile_max : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -569,14 +569,14 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[4], float4_t &c0, 
 #pragma unroll
         for (int db = 0; db < Lds<D>::kDBlocks; ++db) o[db] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[kb] -= delta;
+        for (int kb = 0; kb < KB; ++kb) s[kb] -= delta;
         c0 -= delta;
         m_run = m_new;
-        exp_tile(s, l_run, p);
-        pv_tile<D>(vt, p, o, l16, g4);
+        exp_tile<KB>(s, l_run, p);
+        pv_tile<D, KB>(vt, p, o, l16, g4);
     } else {
-        exp_tile(s, l_run, p);
-        pv_tile<D>(vt, p, o, l16, g4);
+        exp_tile<KB>(s, l_run, p);
+        pv_tile<D, KB>(vt, p, o, l16, g4);
     }
 }
 
@@ -778,6 +778,197 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         if (c + j < io.head_dim) orow[c + j] = y[j];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------- split-key kernel
+// Small grids (at most one 64-row block per CU): 16 waves = 4 row groups x
+// 4 key chunks.  A workgroup owns 64 query rows; the keys stream through
+// LDS in tiles of 128 (double buffered, one barrier per tile, as above) and
+// key chunk c of every tile - rows [32c, 32c + 32) - goes to the waves of
+// chunk c, so each wave keeps its own (m, l, o) over a quarter of the keys
+// (16 rows x 32 keys per tile: two 16-key blocks).  At the end the chunks'
+// states are merged through LDS with the online-softmax rule (scale each
+// by 2^(m_c - m), add) and chunk 0 writes the rows.  This gives 4 waves per
+// SIMD where the 64-row workgroups of the plain kernel give one.
+constexpr int kSplitChunks = 4;
+constexpr int kSplitTileN = 32 * kSplitChunks;  // keys per LDS tile
+constexpr int kSplitBlockM = 64;                // query rows per workgroup
+
+template <int D, bool SPLIT, int IO, typename T>
+__global__ void __launch_bounds__(1024, 4)
+attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                           const T *__restrict__ v, T *__restrict__ out, int n_patches,
+                           int q_blocks, int total_blocks, float lo_window, float lo_gate,
+                           Io io) {
+    using L = Lds<D>;
+    constexpr int WAVES = 16;
+    constexpr int TN = kSplitTileN;
+    constexpr bool KLO = SPLIT && sizeof(T) == 4;
+    __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][TN][L::kKRow];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][TN][L::kKRow];
+    __shared__ __attribute__((aligned(16)))
+    _Float16 kl_s[KLO ? 2 : 1][KLO ? TN : 1][L::kKRow];
+
+    const int logical = xcd_remap(blockIdx.x, total_blocks);
+    const int head = logical / q_blocks;
+    const int qblk = logical - head * q_blocks;
+    const size_t base = IO == kIoDense ? (size_t)head * (size_t)n_patches * D
+                                       : (size_t)((long long)head * io.stride_head);
+    const T *__restrict__ qg = q + base;
+    const T *kg = k + base;
+    const T *vg = v + base;
+    T *__restrict__ og = out + base;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int g4 = lane >> 4;
+    const int rgroup = wave >> 2;  // 16-row group of the workgroup's 64 rows
+    const int chunk = wave & 3;    // 32-key chunk of every tile
+    const int row = qblk * kSplitBlockM + rgroup * kRowsPerWave + l16;
+    const int n_tiles = (n_patches + TN - 1) / TN;
+    const TileMap<D, WAVES, TN> map(tid);
+
+    // Query fragment, as in attention_fwd_kernel.
+    half8_t qh[L::kKSteps];
+    half8_t ql[L::kKSteps];
+    __amdgpu_buffer_rsrc_t rq;
+    if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
+    typedef typename VecOf<T, 4>::type T4;
+#pragma unroll
+    for (int st = 0; st < L::kKSteps; ++st) {
+        float4_t x[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 32 * st + 8 * g4 + 4 * h;
+            if (row < n_patches) {
+                if constexpr (IO == kIoDense)
+                    x[h] = __builtin_convertvector(*reinterpret_cast<const T4 *>(qg + row * D + c),
+                                                   float4_t);
+                else
+                    x[h] = __builtin_convertvector(
+                        load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io), float4_t);
+            }
+            x[h] *= kLog2e;
+        }
+        const half4_t h0 = cvt4(x[0]), h1 = cvt4(x[1]);
+        qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        if constexpr (SPLIT) {
+            const half4_t e0 = cvt4(x[0] - __builtin_convertvector(h0, float4_t));
+            const half4_t e1 = cvt4(x[1] - __builtin_convertvector(h1, float4_t));
+            ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+        } else {
+            ql[st] = qh[st];
+        }
+    }
+
+    const Rope no_rope{nullptr, 0};
+    TileRegs<D, WAVES, T, false, TN> regs;
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
+    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
+    if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, TN, n_patches, map, regs, io);
+    __syncthreads();
+
+    float4_t o[L::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < L::kDBlocks; ++db) o[db] = zero4();
+    float m_run = -__builtin_inff();
+    float l_run = 0.f;
+    float4_t c0 = zero4();
+    const int key_off = 32 * chunk;
+
+    auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        if (t + 1 < n_tiles) {
+            store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
+                                           vt_s[BUF ^ 1], map, no_rope, nullptr, lane);
+            if (t + 2 < n_tiles)
+                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * TN, n_patches, map, regs, io);
+        }
+        const int key_lim = n_patches - t * TN - key_off;
+        if (key_lim > 0) {  // wave-uniform: a chunk past the last key does nothing
+            float4_t s[2];
+            float win = __builtin_inff();
+            if constexpr (SPLIT) {
+                if (m_run != -__builtin_inff())
+                    win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
+            }
+            qk_tile<D, SPLIT, KLO, 2>(kh_s[BUF] + key_off, kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0),
+                                      qh, ql, c0, s, l16, g4, win);
+            if (key_lim < 32)
+                softmax_pv_tile<D, true, 2>(s, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
+                                            l16, g4);
+            else
+                softmax_pv_tile<D, false, 2>(s, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
+                                             l16, g4);
+        }
+        __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, IntTag<0>{});
+        if (t + 1 < n_tiles) step(t + 1, IntTag<1>{});
+    }
+
+    // Merge chunks 1..3 into chunk 0, one at a time, through the (now idle)
+    // K tile buffers: per row group 64 lanes x (16 o + m + l) floats.
+    constexpr int kState = 4 * L::kDBlocks + 2;
+    float *xfer = reinterpret_cast<float *>(&kh_s[0][0][0]) + rgroup * 64 * kState;
+    static_assert(4 * 64 * kState * 4 <= (int)sizeof(kh_s), "merge buffer");
+#pragma unroll 1
+    for (int c = 1; c < kSplitChunks; ++c) {
+        if (chunk == c) {
+#pragma unroll
+            for (int db = 0; db < L::kDBlocks; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xfer[(4 * db + j) * 64 + lane] = o[db][j];
+            xfer[(4 * L::kDBlocks) * 64 + lane] = m_run;
+            xfer[(4 * L::kDBlocks + 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (chunk == 0) {
+            const float m_c = xfer[(4 * L::kDBlocks) * 64 + lane];
+            const float l_c = xfer[(4 * L::kDBlocks + 1) * 64 + lane];
+            const float m_new = fmaxf(m_run, m_c);
+            // m_new is finite: chunk 0 always holds key 0.
+            const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float ac = __builtin_amdgcn_exp2f(m_c - m_new);
+#pragma unroll
+            for (int db = 0; db < L::kDBlocks; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[db][j] = o[db][j] * a0 + xfer[(4 * db + j) * 64 + lane] * ac;
+            l_run = l_run * a0 + l_c * ac;
+            m_run = m_new;
+        }
+        __syncthreads();
+    }
+
+    if (chunk == 0) {
+        const float inv = 1.0f / sum_lane_groups(l_run);
+        if (row < n_patches) {
+            if constexpr (IO == kIoDense) {
+#pragma unroll
+                for (int db = 0; db < L::kDBlocks; ++db)
+                    *reinterpret_cast<T4 *>(og + row * D + 16 * db + 4 * g4) =
+                        __builtin_convertvector(o[db] * inv, T4);
+            } else {
+                T *orow = og + (size_t)row * io.stride_patch;
+#pragma unroll
+                for (int db = 0; db < L::kDBlocks; ++db) {
+                    const int c = 16 * db + 4 * g4;
+                    const T4 y = __builtin_convertvector(o[db] * inv, T4);
+                    if constexpr (IO == kIoVec4) {
+                        if (c < io.head_dim) *reinterpret_cast<T4 *>(orow + c) = y;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (c + j < io.head_dim) orow[c + j] = y[j];
+                    }
                 }
             }
         }

@@ -90,13 +90,29 @@ hipError_t launch(const T *q, const T *k, const T *v, T *out, const LaunchArgs &
         dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, a.stream);
 }
 
+template <int D, bool SPLIT, int IO, typename T>
+hipError_t launch_split_keys(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
+    int n_patches = a.n_patches;
+    int q_blocks = (n_patches + vattn::kSplitBlockM - 1) / vattn::kSplitBlockM;
+    int total_blocks = q_blocks * a.n_heads;
+    float window = a.pol.window, gate = a.pol.gate;
+    vattn::Io io = a.io;
+    void *args[] = {(void *)&q,            (void *)&k,         (void *)&v,
+                    (void *)&out,          (void *)&n_patches, (void *)&q_blocks,
+                    (void *)&total_blocks, (void *)&window,    (void *)&gate,
+                    (void *)&io};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&vattn::attention_fwd_split_kernel<D, SPLIT, IO, T>),
+        dim3((unsigned)total_blocks), dim3(1024), args, 0, a.stream);
+}
+
 // Workgroup size.  16 waves (256 query rows) share each K/V tile among the
 // most queries (least L2 traffic and conversion work per query) and run one
 // per CU: used when they still give every CU a workgroup.  Smaller grids
-// take 8 waves (two workgroups per CU) while those fill the CUs, and 4 waves
-// (64 rows) below that, so that every CU gets work.  The rotary kernels
-// hold more tile registers per thread and skip the 8-wave step: their
-// 8-wave shape would need two workgroups per CU at 128 VGPRs.
+// take 8 waves (two workgroups per CU) while those fill the CUs.  Below
+// that, 64-row workgroups: the split-key kernel (16 waves, 4 per SIMD) while
+// there is at most one per CU, else 4-wave workgroups (two per CU).  The
+// rotary kernels skip the 8-wave and split-key steps.
 template <int D, bool SPLIT, int IO, typename T, bool ROPE>
 hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     const int64_t wide_blocks =
@@ -107,6 +123,11 @@ hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchAr
     if constexpr (!ROPE) {
         if (2 * wide_blocks >= kCusPerDevice)
             return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+        const int64_t small_blocks =
+            (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::kSplitBlockM - 1) /
+                                  vattn::kSplitBlockM);
+        if (small_blocks <= kCusPerDevice)
+            return launch_split_keys<D, SPLIT, IO, T>(q, k, v, out, a);
     }
     return launch<D, 4, SPLIT, IO, T, ROPE>(q, k, v, out, a);
 }

@@ -161,10 +161,12 @@ def test_strided_c_abi_direct(vattn):
     _assert_close(got, oracle.attention_f64(q, k, v), "strided c-abi")
 
 
-# Grids that select each workgroup shape: 16-wave blocks (256 rows) when
-# there are at least 256 of them, 8-wave blocks while 2x that reaches 256,
-# 4-wave blocks (64 rows) below.
-WORKGROUP_SHAPES = [("4 waves", 2, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000)]
+# Grids that select each kernel shape: 16-wave blocks (256 rows) when there
+# are at least 256 of them, 8-wave blocks while 2x that reaches 256; below,
+# 64-row blocks: the split-key kernel while there are at most 256 of them,
+# else 4-wave blocks.
+WORKGROUP_SHAPES = [("split keys", 2, 1000), ("split keys ragged", 3, 333),
+                    ("4 waves", 20, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000)]
 
 
 @pytest.mark.parametrize("label,h,n", WORKGROUP_SHAPES, ids=[s[0] for s in WORKGROUP_SHAPES])
