@@ -432,14 +432,18 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // lie above -lo_window relative to m_ref (lo_window = +inf: every block,
 // -inf: none).  A key whose f16 logit sits more than lo_window below the
 // running max has weight below 2^-lo_window, so the ~2^-11 relative error
-// its q_hi.k_hi logit carries is negligible in the output.  KLO = false
+// its q_hi.k_hi logit carries is negligible in the output.  On a wave's
+// first tile there is no running max yet (m_ref = 0, s holds the logits):
+// a block is corrected when one of its logits exceeds lo_gate in magnitude,
+// the size below which an f16 logit is accurate enough anyway.  KLO = false
 // (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
 template <int D, bool SPLIT, bool KLO, int KB = 4>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
                                         const half8_t (&qh)[Lds<D>::kKSteps],
                                         const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
-                                        float4_t (&s)[KB], int l16, int g4, float lo_window) {
+                                        float4_t (&s)[KB], int l16, int g4, float lo_window,
+                                        bool first = false, float lo_gate = 0.f) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -454,7 +458,9 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const float lane_max = fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3]));
-            if (__ballot(lane_max > -lo_window)) {
+            const float lane_abs = fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
+                                         fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3])));
+            if (__ballot(first ? lane_abs > lo_gate : lane_max > -lo_window)) {
 #pragma unroll
                 for (int st = 0; st < Lds<D>::kKSteps; ++st) {
                     const half8_t a = *reinterpret_cast<const half8_t *>(
@@ -634,6 +640,10 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const int n_tiles = (n_patches + kTileN - 1) / kTileN;
     const TileMap<D, WAVES> map(tid);
 
+    // Tile 0's loads go out first, so their latency overlaps the Q loads'.
+    TileRegs<D, WAVES, T, ROPE> regs;
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
+
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
@@ -685,8 +695,6 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         }
     }
 
-    TileRegs<D, WAVES, T, ROPE> regs;
-    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
     if constexpr (ROPE) {
         // Zero both cos/sin buffers first, so no lane ever reads LDS the
         // copies leave unwritten; then copy tile 0's rows.
@@ -732,15 +740,17 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
             }
         }
         float4_t s[4];
-        // Correction window of the SPLIT kernel: every block of the first
-        // tile (no running max yet); later, lo_window for waves whose running
-        // max has magnitude above lo_gate (large logits), none otherwise.
+        // Correction window of the SPLIT kernel: on the first tile (no
+        // running max yet) the blocks with logits above lo_gate in magnitude;
+        // later, lo_window for waves whose running max has magnitude above
+        // lo_gate (large logits), none otherwise.
         float win = __builtin_inff();
+        const bool first = m_run == -__builtin_inff();
         if constexpr (SPLIT) {
-            if (m_run != -__builtin_inff())
-                win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
+            if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
         }
-        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, l16, g4, win);
+        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, l16, g4, win, first,
+                               lo_gate);
         const int key_lim = n_patches - t * kTileN;
         if (key_lim < kTileN)
             softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
@@ -834,6 +844,10 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const int n_tiles = (n_patches + TN - 1) / TN;
     const TileMap<D, WAVES, TN> map(tid);
 
+    const Rope no_rope{nullptr, 0};
+    TileRegs<D, WAVES, T, false, TN> regs;
+    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
+
     // Query fragment, as in attention_fwd_kernel.
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
@@ -867,9 +881,6 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
         }
     }
 
-    const Rope no_rope{nullptr, 0};
-    TileRegs<D, WAVES, T, false, TN> regs;
-    load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
     store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
     if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, TN, n_patches, map, regs, io);
     __syncthreads();
@@ -894,12 +905,12 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if (key_lim > 0) {  // wave-uniform: a chunk past the last key does nothing
             float4_t s[2];
             float win = __builtin_inff();
+            const bool first = m_run == -__builtin_inff();
             if constexpr (SPLIT) {
-                if (m_run != -__builtin_inff())
-                    win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
+                if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
             }
             qk_tile<D, SPLIT, KLO, 2>(kh_s[BUF] + key_off, kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0),
-                                      qh, ql, c0, s, l16, g4, win);
+                                      qh, ql, c0, s, l16, g4, win, first, lo_gate);
             if (key_lim < 32)
                 softmax_pv_tile<D, true, 2>(s, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
                                             l16, g4);
