@@ -564,10 +564,12 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0,
         mx = fmaxf(fmaxf(mx, s[e / 4][e % 4]), s[(e + 1) / 4][(e + 1) % 4]);
     mx = fmaxf(mx, s[KB - 1][3]);
     const float m_ref = -c0[0];
-    const float tile_max = max_lane_groups(mx) + m_ref;
-    const bool raise = tile_max > m_run + kRescaleSlack;
     half8_t p[KB / 2];
-    if (__ballot(raise)) {
+    // Some lane's own scores exceed the slack: only then is the query's
+    // tile max (across its 4 lane groups) needed.
+    if (__ballot(mx + m_ref > m_run + kRescaleSlack)) {
+        const float tile_max = max_lane_groups(mx) + m_ref;
+        const bool raise = tile_max > m_run + kRescaleSlack;
         const float m_new = raise ? tile_max : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         const float delta = m_new - m_ref;
