@@ -15,13 +15,14 @@
  * patch count).  No scale is applied inside: the caller folds any 1/sqrt(d)
  * into Q, as the shader's Params carries no scale field.
  *
- * Layout: q, k, v and out are float32.  vattn_forward and
- * vattn_forward_precision take the page's head-major layout, C-contiguous
- * [n_heads][n_patches][head_dim]: element (h, i, c) sits at
- * h*n_patches*head_dim + i*head_dim + c.  vattn_forward_strided takes any
- * pair of row strides, e.g. the patch-major [n_patches][n_heads][head_dim]
- * layout a fused QKV projection writes (the sibling of the page's
- * head-major "HPD" buffers).
+ * Layout: q, k, v and out are float32 (float16 for the *_f16 entry
+ * points).  vattn_forward and vattn_forward_precision take the page's
+ * head-major layout, C-contiguous [n_heads][n_patches][head_dim]: element
+ * (h, i, c) sits at h*n_patches*head_dim + i*head_dim + c.
+ * vattn_forward_strided and the f16 / rotary entry points take any pair of
+ * row strides, e.g. the patch-major [n_patches][n_heads][head_dim] layout a
+ * fused QKV projection writes (the sibling of the page's head-major "HPD"
+ * buffers).
  *
  * Numerics: Q, K, V are rounded to f16 (round-to-nearest-even) for the matrix
  * cores and all sums are accumulated in f32, with an online (running max /
@@ -49,7 +50,7 @@ typedef enum vattn_status {
                                 access mode (4 elements: 16 bytes of f32 or
                                 8 of f16; one element when head_dim or a
                                 stride is not a multiple of 4)                */
-    VATTN_ERR_ALIAS = 5,     /* out overlaps q, k or v                       */
+    VATTN_ERR_ALIAS = 5,     /* out overlaps q, k, v or the rotary table     */
     VATTN_ERR_HIP = 6,       /* the HIP runtime refused the launch           */
     VATTN_ERR_ARG = 7,       /* unknown precision mode                       */
     VATTN_ERR_ROPE = 8       /* invalid rotary parameters (rope_dims, base,

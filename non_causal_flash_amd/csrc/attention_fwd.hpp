@@ -1,6 +1,6 @@
 // attention_fwd.hpp - head-major, non-causal flash attention forward for
-// gfx950 (MI355X): f32 in HBM, f16 operands on the matrix cores, f32
-// accumulation, online softmax in registers.
+// gfx950 (MI355X): f32 or f16 tensors in HBM, f16 operands on the matrix
+// cores, f32 accumulation, online softmax in registers.
 //
 // Operation (docs.rs page "rullama 0.1.0", source of
 // src/kernels/wgsl/vision_attention_flash_sub_hpd_f16.wgsl): per head,
@@ -8,26 +8,31 @@
 // [n_heads][n_patches][head_dim].  The page's shader tiles keys in blocks,
 // stages them as f16 in workgroup memory, keeps a running max / running sum
 // per query in f32 and rescales the partial output when the max grows (its
-// key-tile loop and online-softmax update).  This kernel keeps those ideas
-// and re-plans the rest for CDNA4:
+// key-tile loop and online-softmax update).  These kernels keep those ideas
+// and re-plan the rest for CDNA4:
 //
-//  * One workgroup = WAVES waves (8 or 16) of one head; each wave owns 16
-//    query rows, so a wave's state is small enough for 4 waves per SIMD (the
-//    vector ALUs only reach full issue rate with several waves).  The whole
-//    workgroup shares each converted K/V tile, so 16 waves (256 rows) halve
-//    the K/V traffic from L2 and the conversion work per query; 8 waves
-//    (128 rows) give twice as many workgroups for small grids.
-//  * Keys stream through LDS in tiles of 64, double buffered.  Tile t+1 is
-//    loaded into registers with buffer loads (the hardware range check
-//    zero-fills rows past n_patches), converted to f16 with
-//    round-to-nearest-even and stored to the other LDS buffer while tile t
-//    is consumed; one barrier per tile.
+//  * attention_fwd_kernel: one workgroup = WAVES waves (4, 8 or 16) of one
+//    head; each wave owns 16 query rows, so a wave's state is small enough
+//    for 4 waves per SIMD (the vector ALUs only reach full issue rate with
+//    several waves).  The whole workgroup shares each converted K/V tile, so
+//    16 waves (256 rows) cut the K/V traffic from L2 and the conversion work
+//    per query; 8 and 4 waves give more workgroups for smaller grids.
+//  * attention_fwd_split_kernel (small grids): 16 waves = 4 row groups x 4
+//    key chunks over 64 rows, each wave on a quarter of every tile's keys,
+//    the chunks' softmax states merged through LDS at the end.
+//  * Keys stream through LDS in tiles, double buffered.  Tile t+1 is loaded
+//    into registers with buffer loads (the hardware range check zero-fills
+//    rows past n_patches), converted to f16 with round-to-nearest-even and
+//    stored to the other LDS buffer while tile t is consumed; one barrier
+//    per tile.
 //  * Scores are produced transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_f16: the key fragment (A operand) comes from LDS,
 //    the query fragment (B operand) stays in registers.  In the 16x16
-//    accumulator a lane holds 4 keys of ONE query, so the row max / row sum
-//    are in-lane plus two cross-lane steps per tile.  The accumulator starts
-//    at -m (running max), so the matrix core also does the max subtraction.
+//    accumulator a lane holds 4 keys of ONE query, so the max test and the
+//    row sum are in-lane; the query's max across its 4 lane groups (two
+//    permlane swaps) is only needed when the running max is raised, and the
+//    row sum's only once at the end.  The accumulator starts at -m (running
+//    max), so the matrix core also does the max subtraction.
 //  * The probabilities P^T leave the accumulator as the B operand of
 //    O^T = V^T P^T without data movement.  V stays row-major in LDS, like K;
 //    the V^T operand is gathered with the gfx950 LDS transpose load
@@ -35,11 +40,12 @@
 //  * log2(e) is folded into Q, so each exponential is one v_exp_f32 (2^x).
 //    The running max is only raised when a tile's max exceeds it by more than
 //    kRescaleSlack (P <= 2^8 is harmless in f16 and f32); the O/l rescale is
-//    a wave-uniform branch that is rare once the max settles.
+//    a wave-uniform branch.
 //  * The row sum l accumulates the f16-rounded P (v_dot2_f32_f16 against
 //    1.0), i.e. exactly the weights the P.V product uses.
 //  * SPLIT precision: q = q_hi + q_lo, k = k_hi + k_lo (all f16); the score
-//    adds q_lo.k_hi and q_hi.k_lo to q_hi.k_hi in the f32 accumulator.
+//    adds q_lo.k_hi and q_hi.k_lo to q_hi.k_hi in the f32 accumulator, for
+//    every block (SPLIT) or only the blocks where it can matter (AUTO).
 //  * Workgroup ids are remapped so that the query blocks of one head land
 //    on one XCD (dispatch is round-robin over the 8 XCDs), keeping that
 //    head's K/V in one L2.
@@ -51,8 +57,8 @@
 //    zero in every operand (their loads point past the buffer range, which
 //    the hardware returns as 0), so they add nothing to Q.K^T and the
 //    matching output columns are simply not stored.  kIoVec4 moves 4- (or
-//    2-) float vectors (head_dim and strides multiples of 4), kIoScalar
-//    single floats.
+//    2-) element vectors (head_dim and strides multiples of 4), kIoScalar
+//    single elements.
 //  * Optional NeoX rotary transform of Q and K (ROPE; docs.rs page "rullama
 //    0.2.0", src/kernels/wgsl/rope_neox_backward.wgsl, the forward rotation
 //    of its header comment): pairs (x[i], x[i + half]), i < half =
@@ -147,10 +153,6 @@ __device__ __forceinline__ half4_t cvt4(float4_t x) {
     return __builtin_convertvector(x, half4_t);
 }
 
-__device__ __forceinline__ float4_t load4(const float *p) {
-    return *reinterpret_cast<const float4_t *>(p);
-}
-
 __device__ __forceinline__ float4_t zero4() { return (float4_t){0.f, 0.f, 0.f, 0.f}; }
 
 // Max / sum over the 4 lanes {l, l^16, l^32, l^48}, which hold one query's
@@ -240,14 +242,13 @@ struct TileMap {
     }
 };
 
-template <int D, int WAVES, typename T, bool ROPE, int TN = kTileN>
+// One tile's K and V elements of a thread, in flight from HBM to LDS.
+template <int D, int WAVES, typename T, int TN = kTileN>
 struct TileRegs {
     using S = Shape<D, WAVES, TN>;
     typename VecOf<T, S::kKWidth>::type k[S::kKVec];
     typename VecOf<T, S::kKWidth>::type v[S::kKVec];
 };
-
-
 
 // Vector of N elements at columns [col, col+N) of a row (row_off = the
 // row's element offset): the strided modes move columns >= head_dim out of
@@ -336,10 +337,10 @@ __device__ __forceinline__ float lane_fetch(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-template <int D, int WAVES, int IO, typename T, bool ROPE, int TN>
+template <int D, int WAVES, int IO, typename T, int TN>
 __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
                                           int n_patches, const TileMap<D, WAVES, TN> &m,
-                                          TileRegs<D, WAVES, T, ROPE, TN> &r, const Io &io) {
+                                          TileRegs<D, WAVES, T, TN> &r, const Io &io) {
     using S = Shape<D, WAVES, TN>;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, IO>(kg, key0, n_patches, io);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, IO>(vg, key0, n_patches, io);
@@ -356,7 +357,7 @@ __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
 // f32 inputs SPLIT also stores k_lo = f16(k - f32(f16(k))).  f16 inputs
 // are exact in f16 (no k_lo).
 template <int D, int WAVES, bool SPLIT, typename T, bool ROPE, int TN>
-__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, ROPE, TN> &r,
+__device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, TN> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
                                            _Float16 (*vh)[Lds<D>::kKRow],
@@ -643,7 +644,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const TileMap<D, WAVES> map(tid);
 
     // Tile 0's loads go out first, so their latency overlaps the Q loads'.
-    TileRegs<D, WAVES, T, ROPE> regs;
+    TileRegs<D, WAVES, T> regs;
     load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
 
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
@@ -707,7 +708,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         wait_vmem();
         __syncthreads();
     }
-    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
+    store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
     if (n_tiles > 1) {
         load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
         if constexpr (ROPE) {
@@ -731,7 +732,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         // drain while this tile is computed, and the stores have landed long
         // before the barrier.
         if (t + 1 < n_tiles) {
-            store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
+            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
                                            vt_s[BUF ^ 1], map, rope, cs_s[ROPE ? (BUF ^ 1) : 0],
                                            lane);
             if (t + 2 < n_tiles) {
@@ -847,7 +848,7 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const TileMap<D, WAVES, TN> map(tid);
 
     const Rope no_rope{nullptr, 0};
-    TileRegs<D, WAVES, T, false, TN> regs;
+    TileRegs<D, WAVES, T, TN> regs;
     load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
 
     // Query fragment, as in attention_fwd_kernel.
@@ -883,7 +884,7 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
         }
     }
 
-    store_tile<D, WAVES, SPLIT, T>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
+    store_tile<D, WAVES, SPLIT, T, false>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
     if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, TN, n_patches, map, regs, io);
     __syncthreads();
 
@@ -898,7 +899,7 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
         constexpr int BUF = decltype(buf_tag)::value;
         if (t + 1 < n_tiles) {
-            store_tile<D, WAVES, SPLIT, T>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
+            store_tile<D, WAVES, SPLIT, T, false>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
                                            vt_s[BUF ^ 1], map, no_rope, nullptr, lane);
             if (t + 2 < n_tiles)
                 load_tile<D, WAVES, IO>(kg, vg, (t + 2) * TN, n_patches, map, regs, io);

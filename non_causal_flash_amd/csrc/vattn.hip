@@ -241,7 +241,7 @@ extern "C" const char *vattn_status_string(int status) {
         case VATTN_ERR_SIZE: return "invalid or too large size or stride";
         case VATTN_ERR_HEAD_DIM: return "head_dim must be in [1, 64]";
         case VATTN_ERR_ALIGN: return "tensor not aligned for its access mode";
-        case VATTN_ERR_ALIAS: return "out overlaps q, k or v";
+        case VATTN_ERR_ALIAS: return "out overlaps q, k, v or the rotary table";
         case VATTN_ERR_HIP: return "HIP runtime error";
         case VATTN_ERR_ARG: return "unknown precision mode";
         case VATTN_ERR_ROPE: return "invalid rotary parameters";
