@@ -43,6 +43,11 @@
 //    a wave-uniform branch.
 //  * The row sum l accumulates the f16-rounded P (v_dot2_f32_f16 against
 //    1.0), i.e. exactly the weights the P.V product uses.
+//  * A 32-key half of a tile whose scores all lie more than 26 log2 units
+//    below the reference max holds only probabilities that round to 0 in
+//    f16: its exponentials, row-sum terms and P.V products are skipped
+//    (the result is bit for bit the same).  Sharp softmax rows skip about
+//    half of them.
 //  * SPLIT precision: q = q_hi + q_lo, k = k_hi + k_lo (all f16); the score
 //    adds q_lo.k_hi and q_hi.k_lo to q_hi.k_hi in the f32 accumulator, for
 //    every block (SPLIT) or only the blocks where it can matter (AUTO).
@@ -485,57 +490,58 @@ __device__ __forceinline__ half4_t read_tr16(const _Float16 *p) {
     return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)p));
 }
 
-// O^T += V^T P^T for one 64-key tile.  The A operand (16 dims x 32 keys) is
-// two ds_read_b64_tr_b16 of row-major V: in each 16-lane group, lane s
-// points at 4 consecutive dims of one key row and output lane j receives
-// dim j of the 4 keys addressed by lanes j/4, j/4+4, j/4+8, j/4+12.  Lane s
-// of group g addresses key 4g + s/4 (+16 for the second read) at dims
-// 4*(s%4)..+3 of the block, which yields, for lane 16g+j, dim j of keys
-// {4g..4g+3} and {16+4g..16+4g+3}: the keys the P operand of that lane
-// holds, in the same order.
-template <int D, int KB = 4>
-__device__ __forceinline__ void pv_tile(const _Float16 (*vh)[Lds<D>::kKRow],
-                                        const half8_t (&p)[KB / 2],
-                                        float4_t (&o)[Lds<D>::kDBlocks], int l16, int g4) {
+// A probability below 2^-26 is 0 once rounded to f16 (the smallest f16
+// subnormal is 2^-24 and round-to-nearest-even sends everything up to 2^-25
+// to 0), so a score more than 26 log2 units below the reference max adds
+// exactly nothing to l or O.
+constexpr float kDeadBelow = -26.0f;
+
+// Exponentials, row sum and O^T += V^T P^T for one tile, in 32-key halves
+// (two 16-key blocks, one 16x16x32 MFMA k-step each).  A half whose scores
+// all lie below kDeadBelow (a wave-uniform test on the lanes' maxima mxh)
+// contributes exactly 0 and is skipped; sharp softmax rows have many such
+// halves.  Per half: P = 2^s in f16 (RNE), l += the f16-rounded P
+// (v_dot2_f32_f16 against 1.0, i.e. exactly the weights P.V uses), and the
+// P.V product.  The A operand (16 dims x 32 keys) is two
+// ds_read_b64_tr_b16 of row-major V: in each 16-lane group, lane s points
+// at 4 consecutive dims of one key row and output lane j receives dim j of
+// the 4 keys addressed by lanes j/4, j/4+4, j/4+8, j/4+12.  Lane s of group
+// g addresses key 4g + s/4 (+16 for the second read) at dims 4*(s%4)..+3 of
+// the block, which yields, for lane 16g+j, dim j of keys {4g..4g+3} and
+// {16+4g..16+4g+3}: the keys the P operand of that lane holds, in the same
+// order.  The order of every accumulation is the same whether or not other
+// halves are skipped.
+template <int D, int KB>
+__device__ __forceinline__ void exp_pv_live(const float4_t (&s)[KB], const float (&mxh)[KB / 2],
+                                            float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
+                                            const _Float16 (*vh)[Lds<D>::kKRow], int l16,
+                                            int g4) {
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     const int key = 4 * g4 + (l16 >> 2);
     const int dim = 4 * (l16 & 3);
 #pragma unroll
-    for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < KB / 2; ++ks) {
-            const half4_t a0 = read_tr16(&vh[32 * ks + key][16 * db + dim]);
-            const half4_t a1 = read_tr16(&vh[32 * ks + 16 + key][16 * db + dim]);
-            const half8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            o[db] = mfma16(a, p[ks], o[db]);
-        }
-    }
-}
-
-__device__ __forceinline__ float max4(float4_t x) {
-    return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-}
-
-// P = 2^s as f16 MFMA operands (the key order of the S accumulator, matched
-// by vt_pos); l += the f16-rounded P.
-template <int KB = 4>
-__device__ __forceinline__ void exp_tile(const float4_t (&s)[KB], float &l_run,
-                                         half8_t (&p)[KB / 2]) {
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float lsum = l_run;
-#pragma unroll
     for (int ks = 0; ks < KB / 2; ++ks) {
-        half2_t h[4];
+        if (__ballot(mxh[ks] > kDeadBelow)) {
+            half2_t h[4];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const float4_t x = s[2 * ks + hf];
-            h[2 * hf] = cvt2(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
-            h[2 * hf + 1] = cvt2(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+            for (int hf = 0; hf < 2; ++hf) {
+                const float4_t x = s[2 * ks + hf];
+                h[2 * hf] = cvt2(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
+                h[2 * hf + 1] = cvt2(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2(h[j], ones, l_run, false);
+            const half8_t p = {h[0][0], h[0][1], h[1][0], h[1][1],
+                               h[2][0], h[2][1], h[3][0], h[3][1]};
+#pragma unroll
+            for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
+                const half4_t a0 = read_tr16(&vh[32 * ks + key][16 * db + dim]);
+                const half4_t a1 = read_tr16(&vh[32 * ks + 16 + key][16 * db + dim]);
+                const half8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                o[db] = mfma16(a, p, o[db]);
+            }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lsum = __builtin_amdgcn_fdot2(h[j], ones, lsum, false);
-        p[ks] = (half8_t){h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
     }
-    l_run = lsum;
 }
 
 // Online softmax and P.V for one tile whose scores s hold s_true - m_run
@@ -543,9 +549,9 @@ __device__ __forceinline__ void exp_tile(const float4_t (&s)[KB], float &l_run,
 // m_run = -inf and c0 = 0).  The running max is raised only when the tile's
 // max exceeds it by more than kRescaleSlack: then o and l are scaled by
 // 2^(m_old - m_new), s is rebased and c0 follows.  That branch is
-// wave-uniform and rare once the max settles; it carries its own copy of
-// the exponentials and the P.V product, so the common path joins the rare
-// one only after values both sides compute afresh (no register copies).
+// wave-uniform; it carries its own copy of the exponentials and the P.V
+// product, so the common path joins the rare one only after values both
+// sides compute afresh (no register copies).
 template <int D, bool MASK, int KB = 4>
 __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0, float &m_run,
                                                 float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
@@ -558,14 +564,21 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0,
             for (int i = 0; i < 4; ++i)
                 if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
     }
-    // In-lane max over the KB x 4 scores, as a chain of 3-input maxima.
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    // In-lane maxima of the two 16-key blocks of each 32-key half, as
+    // chains of 3-input maxima, and over the tile.
+    float mxh[KB / 2];
 #pragma unroll
-    for (int e = 3; e + 1 < 4 * KB; e += 2)
-        mx = fmaxf(fmaxf(mx, s[e / 4][e % 4]), s[(e + 1) / 4][(e + 1) % 4]);
-    mx = fmaxf(mx, s[KB - 1][3]);
+    for (int ks = 0; ks < KB / 2; ++ks) {
+        const float4_t x = s[2 * ks], y = s[2 * ks + 1];
+        float h = fmaxf(fmaxf(x[0], x[1]), x[2]);
+        h = fmaxf(fmaxf(h, x[3]), y[0]);
+        h = fmaxf(fmaxf(h, y[1]), y[2]);
+        mxh[ks] = fmaxf(h, y[3]);
+    }
+    float mx = mxh[0];
+#pragma unroll
+    for (int ks = 1; ks < KB / 2; ++ks) mx = fmaxf(mx, mxh[ks]);
     const float m_ref = -c0[0];
-    half8_t p[KB / 2];
     // Some lane's own scores exceed the slack: only then is the query's
     // tile max (across its 4 lane groups) needed.
     if (__ballot(mx + m_ref > m_run + kRescaleSlack)) {
@@ -579,13 +592,13 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0,
         for (int db = 0; db < Lds<D>::kDBlocks; ++db) o[db] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s[kb] -= delta;
+#pragma unroll
+        for (int ks = 0; ks < KB / 2; ++ks) mxh[ks] -= delta;
         c0 -= delta;
         m_run = m_new;
-        exp_tile<KB>(s, l_run, p);
-        pv_tile<D, KB>(vt, p, o, l16, g4);
+        exp_pv_live<D, KB>(s, mxh, l_run, o, vt, l16, g4);
     } else {
-        exp_tile<KB>(s, l_run, p);
-        pv_tile<D, KB>(vt, p, o, l16, g4);
+        exp_pv_live<D, KB>(s, mxh, l_run, o, vt, l16, g4);
     }
 }
 
