@@ -443,13 +443,19 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // a block is corrected when one of its logits exceeds lo_gate in magnitude,
 // the size below which an f16 logit is accurate enough anyway.  KLO = false
 // (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
+//
+// bmax[kb] receives the lane's maximum over block kb before any correction
+// (the softmax reuses it: a correction moves a score by ~2^-11 of its size,
+// which matters for no reference-max or dead-block decision, and blocks in
+// the correction window are never dead).
 template <int D, bool SPLIT, bool KLO, int KB = 4>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
                                         const half8_t (&qh)[Lds<D>::kKSteps],
                                         const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
-                                        float4_t (&s)[KB], int l16, int g4, float lo_window,
-                                        bool first = false, float lo_gate = 0.f) {
+                                        float4_t (&s)[KB], float (&bmax)[KB], int l16, int g4,
+                                        float lo_window, bool first = false,
+                                        float lo_gate = 0.f) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -459,26 +465,36 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
             s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
         }
     }
-    // lo_window is wave-uniform: skip the block tests when no block can pass.
-    if (SPLIT && lo_window != -__builtin_inff()) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const float lane_max = fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3]));
-            const float lane_abs = fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
-                                         fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3])));
-            if (__ballot(first ? lane_abs > lo_gate : lane_max > -lo_window)) {
+    for (int kb = 0; kb < KB; ++kb)
+        bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
+    auto correct = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-                for (int st = 0; st < Lds<D>::kKSteps; ++st) {
-                    const half8_t a = *reinterpret_cast<const half8_t *>(
-                        &kh[16 * kb + l16][32 * st + 8 * g4]);
-                    s[kb] = mfma16(a, ql[st], s[kb]);
-                    if constexpr (KLO) {
-                        const half8_t al = *reinterpret_cast<const half8_t *>(
-                            &kl[16 * kb + l16][32 * st + 8 * g4]);
-                        s[kb] = mfma16(al, qh[st], s[kb]);
-                    }
-                }
+        for (int st = 0; st < Lds<D>::kKSteps; ++st) {
+            const half8_t a = *reinterpret_cast<const half8_t *>(
+                &kh[16 * kb + l16][32 * st + 8 * g4]);
+            s[kb] = mfma16(a, ql[st], s[kb]);
+            if constexpr (KLO) {
+                const half8_t al = *reinterpret_cast<const half8_t *>(
+                    &kl[16 * kb + l16][32 * st + 8 * g4]);
+                s[kb] = mfma16(al, qh[st], s[kb]);
             }
+        }
+    };
+    // lo_window and first are wave-uniform: skip the block tests when no
+    // block can pass, and test magnitudes only on the first tile.
+    if (SPLIT && lo_window != -__builtin_inff()) {
+        if (first) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float lane_abs = fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
+                                             fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3])));
+                if (__ballot(lane_abs > lo_gate)) correct(kb);
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                if (__ballot(bmax[kb] > -lo_window)) correct(kb);
         }
     }
 }
@@ -553,28 +569,25 @@ __device__ __forceinline__ void exp_pv_live(const float4_t (&s)[KB], const float
 // product, so the common path joins the rare one only after values both
 // sides compute afresh (no register copies).
 template <int D, bool MASK, int KB = 4>
-__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float4_t &c0, float &m_run,
-                                                float &l_run, float4_t (&o)[Lds<D>::kDBlocks],
+__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)[KB], float4_t &c0,
+                                                float &m_run, float &l_run,
+                                                float4_t (&o)[Lds<D>::kDBlocks],
                                                 const _Float16 (*vt)[Lds<D>::kKRow],
                                                 int key_lim, int l16, int g4) {
     if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
+            bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
+        }
     }
-    // In-lane maxima of the two 16-key blocks of each 32-key half, as
-    // chains of 3-input maxima, and over the tile.
+    // In-lane maxima of each 32-key half (from the blocks' maxima of
+    // qk_tile) and over the tile.
     float mxh[KB / 2];
 #pragma unroll
-    for (int ks = 0; ks < KB / 2; ++ks) {
-        const float4_t x = s[2 * ks], y = s[2 * ks + 1];
-        float h = fmaxf(fmaxf(x[0], x[1]), x[2]);
-        h = fmaxf(fmaxf(h, x[3]), y[0]);
-        h = fmaxf(fmaxf(h, y[1]), y[2]);
-        mxh[ks] = fmaxf(h, y[3]);
-    }
+    for (int ks = 0; ks < KB / 2; ++ks) mxh[ks] = fmaxf(bmax[2 * ks], bmax[2 * ks + 1]);
     float mx = mxh[0];
 #pragma unroll
     for (int ks = 1; ks < KB / 2; ++ks) mx = fmaxf(mx, mxh[ks]);
@@ -756,6 +769,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
             }
         }
         float4_t s[4];
+        float bmax[4];
         // Correction window of the SPLIT kernel: on the first tile (no
         // running max yet) the blocks with logits above lo_gate in magnitude;
         // later, lo_window for waves whose running max has magnitude above
@@ -765,13 +779,13 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if constexpr (SPLIT) {
             if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
         }
-        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, l16, g4, win, first,
+        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, bmax, l16, g4, win, first,
                                lo_gate);
         const int key_lim = n_patches - t * kTileN;
         if (key_lim < kTileN)
-            softmax_pv_tile<D, true>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+            softmax_pv_tile<D, true>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
         else
-            softmax_pv_tile<D, false>(s, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+            softmax_pv_tile<D, false>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
         // ROPE: this wave's cos/sin copies must have landed before the
         // barrier that hands them to every wave.
         if constexpr (ROPE) wait_vmem();
@@ -920,18 +934,19 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
         const int key_lim = n_patches - t * TN - key_off;
         if (key_lim > 0) {  // wave-uniform: a chunk past the last key does nothing
             float4_t s[2];
+            float bmax[2];
             float win = __builtin_inff();
             const bool first = m_run == -__builtin_inff();
             if constexpr (SPLIT) {
                 if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
             }
             qk_tile<D, SPLIT, KLO, 2>(kh_s[BUF] + key_off, kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0),
-                                      qh, ql, c0, s, l16, g4, win, first, lo_gate);
+                                      qh, ql, c0, s, bmax, l16, g4, win, first, lo_gate);
             if (key_lim < 32)
-                softmax_pv_tile<D, true, 2>(s, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
+                softmax_pv_tile<D, true, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
                                             l16, g4);
             else
-                softmax_pv_tile<D, false, 2>(s, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
+                softmax_pv_tile<D, false, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
                                              l16, g4);
         }
         __syncthreads();
