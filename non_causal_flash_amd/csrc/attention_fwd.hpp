@@ -568,7 +568,10 @@ __device__ __forceinline__ void exp_pv_live(const float4_t (&s)[KB], const float
 // wave-uniform; it carries its own copy of the exponentials and the P.V
 // product, so the common path joins the rare one only after values both
 // sides compute afresh (no register copies).
-template <int D, bool MASK, int KB = 4>
+// RECOMPUTE: take the blocks' maxima afresh from s instead of keeping
+// qk_tile's across the corrections (fewer live registers, for kernels that
+// are short of them).
+template <int D, bool MASK, int KB = 4, bool RECOMPUTE = false>
 __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)[KB], float4_t &c0,
                                                 float &m_run, float &l_run,
                                                 float4_t (&o)[Lds<D>::kDBlocks],
@@ -576,12 +579,15 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)
                                                 int key_lim, int l16, int g4) {
     if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
+    }
+    if constexpr (MASK || RECOMPUTE) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
             bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
-        }
     }
     // In-lane maxima of each 32-key half (from the blocks' maxima of
     // qk_tile) and over the tile.
@@ -783,9 +789,11 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                lo_gate);
         const int key_lim = n_patches - t * kTileN;
         if (key_lim < kTileN)
-            softmax_pv_tile<D, true>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+            softmax_pv_tile<D, true, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16,
+                                              g4);
         else
-            softmax_pv_tile<D, false>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16, g4);
+            softmax_pv_tile<D, false, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim,
+                                               l16, g4);
         // ROPE: this wave's cos/sin copies must have landed before the
         // barrier that hands them to every wave.
         if constexpr (ROPE) wait_vmem();
