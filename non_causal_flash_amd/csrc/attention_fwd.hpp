@@ -73,9 +73,10 @@
 //    f16 rounding (and the hi/lo split), so rotated K never goes to HBM.
 //    A tile thread holds the columns it loaded; the other half of each pair
 //    sits in a lane of the same row (half/width lanes away) and is fetched
-//    with ds_bpermute.  The tile's cos/sin rows (one contiguous slice of the
-//    table) are copied global -> LDS by buffer loads with an LDS
-//    destination, one tile ahead like K and V, so they take no registers.
+//    with ds_bpermute.  Each wave copies the cos/sin rows its own lanes
+//    rotate (one contiguous piece of the table, at most 1 KB per load)
+//    global -> LDS with a buffer load that has an LDS destination, one tile
+//    ahead like K and V: no registers, and no other wave waits for it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -302,24 +303,34 @@ struct CsTile {
     static constexpr int kFloats = kTileN * (D / 2) * 2;
 };
 
-// Issue the copy of the table rows [key0, key0 + kTileN) into `dst` (LDS):
-// 1 KB per wave instruction (64 lanes x 16 bytes, lane l at byte 16 l), the
-// slice's 512*half bytes split over the waves.  Rows past n_patches read 0.
-template <int WAVES>
-__device__ __forceinline__ void copy_cs_tile(const Rope &rope, int key0, int n_patches,
+// Issue the copy of the table rows this wave's lanes rotate in the tile at
+// key0 into `dst` (LDS, same [row][pair] layout as the table): for each
+// load u, the wave's lanes cover 64 / (D/width) consecutive rows starting at
+// its first lane's row, at most 1 KB of (cos, sin) pairs, copied by one
+// buffer load with an LDS destination (lane l moves 16 bytes to byte 16 l).
+// Each wave reads only rows it copied, so a wait on its own vector-memory
+// counter (wait_vmem) makes them visible; no barrier is involved.  Rows past
+// n_patches read 0.
+template <int D, int WAVES>
+__device__ __forceinline__ void copy_cs_rows(const Rope &rope, int key0, int n_patches,
                                              float *dst, int wave, int lane) {
+    using M = TileMap<D, WAVES>;
+    constexpr int kRows = 64 / M::kPerRow;  // rows per wave and load
     const __amdgpu_buffer_rsrc_t r = rope_rsrc(rope, key0, n_patches);
-    const int chunks = rope.half / 2;  // 1 KB chunks
+    const int lanes = kRows * rope.half / 2;  // 16-byte pieces: <= 64
     // The LDS destination (M0) must be wave-uniform.
-    for (int c = __builtin_amdgcn_readfirstlane(wave); c < chunks; c += WAVES)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void *)(dst + 256 * c), 16, 1024 * c + 16 * lane,
-            0, 0, 0);
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int u = 0; u < Shape<D, WAVES>::kKVec; ++u) {
+        const int row = w * kRows + u * M::kRowStep;
+        if (lane < lanes)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void *)(dst + row * rope.half * 2), 16,
+                row * rope.half * 8 + 16 * lane, 0, 0, 0);
+    }
 }
 
-// The tile loads of a step have landed (registers and LDS copies): all
-// vector-memory counters of this wave drained.  Before a barrier this makes
-// the LDS copies of every wave visible to every wave.
+// All vector-memory loads of this wave have landed, LDS copies included.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 // NeoX rotation of 4 columns of one side of the pairs: x holds this side, y
@@ -385,6 +396,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, TN> &r,
     bool first = false, rotated = false;
     int partner = lane, pair_i = 0;
     if constexpr (ROPE) {
+        wait_vmem();  // this wave's cos/sin copies (and the tile's loads) have landed
         first = m.col < rope.half;
         rotated = m.col < 2 * rope.half;
         const int shift = rope.half / S::kKWidth;
@@ -731,22 +743,18 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     }
 
     if constexpr (ROPE) {
-        // Zero both cos/sin buffers first, so no lane ever reads LDS the
-        // copies leave unwritten; then copy tile 0's rows.
+        // Zero both cos/sin buffers first (a barrier orders these stores
+        // before every wave's copies), so no lane ever reads LDS the copies
+        // leave unwritten; then copy tile 0's rows.
         for (int i = tid; i < 2 * CsTile<D>::kFloats / 4; i += 64 * WAVES)
             reinterpret_cast<float4_t *>(&cs_s[0][0])[i] = zero4();
         __syncthreads();
-        copy_cs_tile<WAVES>(rope, 0, n_patches, cs_s[0], wave, lane);
-        wait_vmem();
-        __syncthreads();
+        copy_cs_rows<D, WAVES>(rope, 0, n_patches, cs_s[0], wave, lane);
     }
     store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
     if (n_tiles > 1) {
         load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
-        if constexpr (ROPE) {
-            copy_cs_tile<WAVES>(rope, kTileN, n_patches, cs_s[1], wave, lane);
-            wait_vmem();
-        }
+        if constexpr (ROPE) copy_cs_rows<D, WAVES>(rope, kTileN, n_patches, cs_s[1], wave, lane);
     }
     __syncthreads();
 
@@ -771,7 +779,8 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
                 // cos/sin of tile t+2 into the buffer tile t's store read.
                 if constexpr (ROPE)
-                    copy_cs_tile<WAVES>(rope, (t + 2) * kTileN, n_patches, cs_s[BUF], wave, lane);
+                    copy_cs_rows<D, WAVES>(rope, (t + 2) * kTileN, n_patches, cs_s[BUF], wave,
+                                           lane);
             }
         }
         float4_t s[4];
@@ -794,9 +803,6 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         else
             softmax_pv_tile<D, false, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim,
                                                l16, g4);
-        // ROPE: this wave's cos/sin copies must have landed before the
-        // barrier that hands them to every wave.
-        if constexpr (ROPE) wait_vmem();
         __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {
