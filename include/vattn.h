@@ -72,8 +72,9 @@ typedef enum vattn_status {
  *        (log2 units, i.e. weight 2^-16) of its query's running maximum, and
  *        only for query groups whose running maximum exceeds 24 log2 units in
  *        magnitude (where the f16 logit error ~2^-11 |logit| becomes
- *        visible); on the first key tile, before a running maximum exists,
- *        the blocks holding a logit above 24 in magnitude.  Same accuracy as
+ *        visible); on a query group's first key tile, before a running
+ *        maximum exists, every block when some logit of the group exceeds
+ *        24 in magnitude.  Same accuracy as
  *        SPLIT on sharp softmax rows at a fraction of its cost.  Inputs whose
  *        logits are small only through cancellation of large |q| |k| should
  *        use SPLIT.

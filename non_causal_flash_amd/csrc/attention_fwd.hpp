@@ -452,14 +452,45 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
 // running max has weight below 2^-lo_window, so the ~2^-11 relative error
 // its q_hi.k_hi logit carries is negligible in the output.  On a wave's
 // first tile there is no running max yet (m_ref = 0, s holds the logits):
-// a block is corrected when one of its logits exceeds lo_gate in magnitude,
-// the size below which an f16 logit is accurate enough anyway.  KLO = false
+// every block is corrected when some logit of the wave exceeds lo_gate in
+// magnitude (the size below which f16 logits are accurate enough), none
+// otherwise.  KLO = false
 // (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
 //
 // bmax[kb] receives the lane's maximum over block kb before any correction
 // (the softmax reuses it: a correction moves a score by ~2^-11 of its size,
 // which matters for no reference-max or dead-block decision, and blocks in
 // the correction window are never dead).
+// q_lo.k_hi (+ q_hi.k_lo) added to the scores of 16-key block kb.
+template <int D, bool KLO, int KB>
+__device__ __forceinline__ void qk_correct(const _Float16 (*kh)[Lds<D>::kKRow],
+                                           const _Float16 (*kl)[Lds<D>::kKRow],
+                                           const half8_t (&qh)[Lds<D>::kKSteps],
+                                           const half8_t (&ql)[Lds<D>::kKSteps],
+                                           float4_t (&s)[KB], int kb, int l16, int g4) {
+#pragma unroll
+    for (int st = 0; st < Lds<D>::kKSteps; ++st) {
+        const half8_t a = *reinterpret_cast<const half8_t *>(&kh[16 * kb + l16][32 * st + 8 * g4]);
+        s[kb] = mfma16(a, ql[st], s[kb]);
+        if constexpr (KLO) {
+            const half8_t al = *reinterpret_cast<const half8_t *>(
+                &kl[16 * kb + l16][32 * st + 8 * g4]);
+            s[kb] = mfma16(al, qh[st], s[kb]);
+        }
+    }
+}
+
+// In-lane maximum magnitude of the scores.
+template <int KB>
+__device__ __forceinline__ float lane_abs_max(const float4_t (&s)[KB]) {
+    float a = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
+                           fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3]))));
+    return a;
+}
+
 template <int D, bool SPLIT, bool KLO, int KB = 4>
 __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
                                         const _Float16 (*kl)[Lds<D>::kKRow],
@@ -481,27 +512,18 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
     for (int kb = 0; kb < KB; ++kb)
         bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
     auto correct = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int st = 0; st < Lds<D>::kKSteps; ++st) {
-            const half8_t a = *reinterpret_cast<const half8_t *>(
-                &kh[16 * kb + l16][32 * st + 8 * g4]);
-            s[kb] = mfma16(a, ql[st], s[kb]);
-            if constexpr (KLO) {
-                const half8_t al = *reinterpret_cast<const half8_t *>(
-                    &kl[16 * kb + l16][32 * st + 8 * g4]);
-                s[kb] = mfma16(al, qh[st], s[kb]);
-            }
-        }
+        qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
     };
     // lo_window and first are wave-uniform: skip the block tests when no
     // block can pass, and test magnitudes only on the first tile.
     if (SPLIT && lo_window != -__builtin_inff()) {
         if (first) {
+            // No running max yet: if any logit of the wave exceeds lo_gate
+            // in magnitude, the tile's keys near each query's maximum are
+            // not known before the cross-lane max, so correct every block.
+            if (__ballot(lane_abs_max(s) > lo_gate)) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float lane_abs = fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
-                                             fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3])));
-                if (__ballot(lane_abs > lo_gate)) correct(kb);
+                for (int kb = 0; kb < KB; ++kb) correct(kb);
             }
         } else {
 #pragma unroll
@@ -866,6 +888,10 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][TN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
     _Float16 kl_s[KLO ? 2 : 1][KLO ? TN : 1][L::kKRow];
+    // SPLIT/AUTO gate of every wave, [step parity][row group][key chunk]: a
+    // chunk sees only a quarter of the keys, so whether a row group's logits
+    // are large enough for corrections is decided from all four chunks.
+    __shared__ __attribute__((aligned(16))) int gate_s[2][4][kSplitChunks];
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
@@ -946,22 +972,50 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 load_tile<D, WAVES, IO>(kg, vg, (t + 2) * TN, n_patches, map, regs, io);
         }
         const int key_lim = n_patches - t * TN - key_off;
-        if (key_lim > 0) {  // wave-uniform: a chunk past the last key does nothing
-            float4_t s[2];
-            float bmax[2];
-            float win = __builtin_inff();
-            const bool first = m_run == -__builtin_inff();
-            if constexpr (SPLIT) {
-                if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
+        const bool live = key_lim > 0;  // wave-uniform: a chunk past the last key does nothing
+        const _Float16(*kh)[L::kKRow] = kh_s[BUF] + key_off;
+        const _Float16(*kl)[L::kKRow] = kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0);
+        float4_t s[2];
+        float bmax[2];
+        // Row-group gate of the SPLIT kernel, shared by its 4 key chunks.
+        // First tile: every block is corrected if some logit of the row
+        // group exceeds lo_gate in magnitude (exchanged behind one extra
+        // barrier).  Later tiles: the lo_window test, relative to the
+        // chunk's own running max (never above the row group's, so the test
+        // includes every key within lo_window of the true max), in row
+        // groups where some chunk's running max exceeds lo_gate in
+        // magnitude (flags written at the end of the previous step).
+        if constexpr (SPLIT) {
+            if (t == 0) {
+                if (live) qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4,
+                                                    -__builtin_inff());
+                const bool big = live && __ballot(lane_abs_max(s) > lo_gate);
+                if (lane == 0) gate_s[1][rgroup][chunk] = big;
+                __syncthreads();
+                const int4 f = *reinterpret_cast<const int4 *>(&gate_s[1][rgroup][0]);
+                if (live && (f.x | f.y | f.z | f.w)) {
+                    qk_correct<D, KLO, 2>(kh, kl, qh, ql, s, 0, l16, g4);
+                    qk_correct<D, KLO, 2>(kh, kl, qh, ql, s, 1, l16, g4);
+                }
+            } else if (live) {
+                const int4 f = *reinterpret_cast<const int4 *>(&gate_s[(t - 1) & 1][rgroup][0]);
+                const float win = (f.x | f.y | f.z | f.w) ? lo_window : -__builtin_inff();
+                qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4, win);
             }
-            qk_tile<D, SPLIT, KLO, 2>(kh_s[BUF] + key_off, kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0),
-                                      qh, ql, c0, s, bmax, l16, g4, win, first, lo_gate);
+        } else if (live) {
+            qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4, -__builtin_inff());
+        }
+        if (live) {
             if (key_lim < 32)
                 softmax_pv_tile<D, true, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
                                             l16, g4);
             else
                 softmax_pv_tile<D, false, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
                                              l16, g4);
+        }
+        if constexpr (SPLIT) {
+            if (lane == 0)
+                gate_s[t & 1][rgroup][chunk] = m_run != -__builtin_inff() && fabsf(m_run) > lo_gate;
         }
         __syncthreads();
     };

@@ -208,3 +208,42 @@ def test_one_hip_runtime_in_process(vattn):
     import re
     maps = open("/proc/self/maps").read()
     assert len(set(re.findall(r"\S*libamdhip64\S*", maps))) == 1
+
+
+# FAST rounds q*log2(e) to f16 (relative error ~2^-12 on every logit), which
+# over the 8-nat gap below moves the small weights by ~0.2%: its case uses
+# values of 100 on them and scales the other values by 10; the corrected
+# modes use 1000 and 1.
+@pytest.mark.parametrize("precision,big,base", [("fast", 100.0, 10.0), ("auto", 1000.0, 1.0),
+                                                ("split", 1000.0, 1.0)])
+def test_small_but_live_key_halves_are_kept(vattn, precision, big, base):
+    """Only the first 32 keys sit at the maximum logit (20).  Every fourth
+    32-key half from the second on holds logits 8 nats lower (weights ~e^-8
+    relative: small, but normal f16 numbers, far above the 2^-26 below which
+    a half is skipped) with large values (`big`): dropping those halves would
+    move the output by ~1.3 (0.13 for FAST's smaller values).  Halves 30 nats lower (probabilities that round to zero
+    in f16) and 15 nats lower sit in between.  Exact float64 oracle; usual
+    tolerance."""
+    h, n, d = 2, 512, 64
+    rng = np.random.default_rng(71)
+    q = np.zeros((h, n, d), np.float32)
+    q[:, :, 0] = 1.0
+    k = (rng.standard_normal((h, n, d)) * 0.05).astype(np.float32)
+    v = (rng.standard_normal((h, n, d)) * base).astype(np.float32)
+    for half in range(n // 32):
+        keys = slice(32 * half, 32 * half + 32)
+        if half == 0:
+            k[:, keys, 0] = 20.0                # the maximum
+        elif half % 4 == 1:
+            k[:, keys, 0] = 12.0                # small but live
+            v[:, keys, :] = big
+        elif half % 4 == 3:
+            k[:, keys, 0] = -10.0               # zero in f16
+            v[:, keys, :] = big
+        else:
+            k[:, keys, 0] = 5.0
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out = vattn.forward(dq, dk, dv, precision=precision)
+    torch.cuda.synchronize()
+    ref = oracle.attention_f64(q, k, v)
+    _assert_close(out.cpu().numpy(), ref, "small live halves %s" % precision)
