@@ -74,10 +74,13 @@ typedef enum vattn_status {
  *        magnitude (where the f16 logit error ~2^-11 |logit| becomes
  *        visible); on a query group's first key tile, before a running
  *        maximum exists, every block when some logit of the group exceeds
- *        24 in magnitude.  Same accuracy as
- *        SPLIT on sharp softmax rows at a fraction of its cost.  Inputs whose
- *        logits are small only through cancellation of large |q| |k| should
- *        use SPLIT.
+ *        24 in magnitude.  Same accuracy as SPLIT on sharp softmax rows at a
+ *        fraction of its cost.  The decision uses the running maximum known
+ *        when a block is processed: keys seen while a group's maximum was
+ *        still below 24 in magnitude keep f16 logits (weights off by up to
+ *        ~1%), which matters only if many of them end up close to a larger
+ *        maximum found later.  Such orderings, and logits that are small only
+ *        through cancellation of large |q| |k|, call for SPLIT.
  */
 typedef enum vattn_precision {
     VATTN_PRECISION_AUTO = 0,
