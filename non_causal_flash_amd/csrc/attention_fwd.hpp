@@ -690,10 +690,16 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // k_lo tiles: f32 K, or rotated K (f16 inputs are exact in f16 only
     // before the rotation).
     constexpr bool KLO = SPLIT && (sizeof(T) == 4 || ROPE);
-    __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][kTileN][L::kKRow];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][kTileN][L::kKRow];
+    // LDS buffers of K/V tiles.  One workgroup per CU (16 waves, no rotary
+    // tables) has room for four: tiles are stored two steps ahead and one
+    // barrier follows every second step.  Otherwise two: one step ahead, a
+    // barrier after every step.
+    constexpr int NB = (WAVES == 16 && !ROPE) ? 4 : 2;
+    constexpr int AHEAD = NB / 2;
+    __shared__ __attribute__((aligned(16))) _Float16 kh_s[NB][kTileN][L::kKRow];
+    __shared__ __attribute__((aligned(16))) _Float16 vt_s[NB][kTileN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
-    _Float16 kl_s[KLO ? 2 : 1][KLO ? kTileN : 1][L::kKRow];
+    _Float16 kl_s[KLO ? NB : 1][KLO ? kTileN : 1][L::kKRow];
     __shared__ __attribute__((aligned(16))) float cs_s[ROPE ? 2 : 1][ROPE ? CsTile<D>::kFloats : 4];
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
@@ -784,6 +790,13 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
         if constexpr (ROPE) copy_cs_rows<D, WAVES>(rope, kTileN, n_patches, cs_s[1], wave, lane);
     }
+    if constexpr (AHEAD == 2) {
+        if (n_tiles > 1) {
+            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[1], kl_s[KLO ? 1 : 0], vt_s[1], map,
+                                                 rope, cs_s[0], lane);
+            if (n_tiles > 2) load_tile<D, WAVES, IO>(kg, vg, 2 * kTileN, n_patches, map, regs, io);
+        }
+    }
     __syncthreads();
 
     float4_t o[L::kDBlocks];
@@ -793,21 +806,27 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     float l_run = 0.f;
     float4_t c0 = zero4();  // -(reference max) seeding every QK accumulator
 
-    auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
-        constexpr int BUF = decltype(buf_tag)::value;
-        // Tile t+1 (in registers since the previous step) into the LDS buffer
-        // tile t-1 used, then the loads of tile t+2: issued at the start, they
-        // drain while this tile is computed, and the stores have landed long
-        // before the barrier.
-        if (t + 1 < n_tiles) {
-            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
-                                           vt_s[BUF ^ 1], map, rope, cs_s[ROPE ? (BUF ^ 1) : 0],
-                                           lane);
-            if (t + 2 < n_tiles) {
-                load_tile<D, WAVES, IO>(kg, vg, (t + 2) * kTileN, n_patches, map, regs, io);
+    // Step t (odd_tag: t is odd).  Tile t + AHEAD (in registers since the
+    // previous step) goes into LDS buffer (t + AHEAD) % NB, then the loads of
+    // the tile after it are issued: they drain while this tile is computed,
+    // and the stores have landed long before the next barrier.  The buffer a
+    // store overwrites was read AHEAD steps earlier, before the last barrier
+    // every wave has passed; a tile stored in step t is read in step
+    // t + AHEAD, after the barrier that ends the group of AHEAD steps
+    // holding step t.
+    auto step = [&](int t, auto odd_tag) __attribute__((always_inline)) {
+        constexpr int ODD = decltype(odd_tag)::value;
+        const int rb = NB == 2 ? ODD : (t & 3);          // buffer of tile t
+        const int wb = NB == 2 ? ODD ^ 1 : ((t + 2) & 3);  // buffer of tile t + AHEAD
+        if (t + AHEAD < n_tiles) {
+            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[wb], kl_s[KLO ? wb : 0], vt_s[wb], map,
+                                                 rope, cs_s[ROPE ? wb : 0], lane);
+            if (t + AHEAD + 1 < n_tiles) {
+                load_tile<D, WAVES, IO>(kg, vg, (t + AHEAD + 1) * kTileN, n_patches, map, regs,
+                                        io);
                 // cos/sin of tile t+2 into the buffer tile t's store read.
                 if constexpr (ROPE)
-                    copy_cs_rows<D, WAVES>(rope, (t + 2) * kTileN, n_patches, cs_s[BUF], wave,
+                    copy_cs_rows<D, WAVES>(rope, (t + 2) * kTileN, n_patches, cs_s[rb], wave,
                                            lane);
             }
         }
@@ -822,16 +841,16 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if constexpr (SPLIT) {
             if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
         }
-        qk_tile<D, SPLIT, KLO>(kh_s[BUF], kl_s[KLO ? BUF : 0], qh, ql, c0, s, bmax, l16, g4, win, first,
-                               lo_gate);
+        qk_tile<D, SPLIT, KLO>(kh_s[rb], kl_s[KLO ? rb : 0], qh, ql, c0, s, bmax, l16, g4, win,
+                               first, lo_gate);
         const int key_lim = n_patches - t * kTileN;
         if (key_lim < kTileN)
-            softmax_pv_tile<D, true, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim, l16,
+            softmax_pv_tile<D, true, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[rb], key_lim, l16,
                                               g4);
         else
-            softmax_pv_tile<D, false, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[BUF], key_lim,
+            softmax_pv_tile<D, false, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[rb], key_lim,
                                                l16, g4);
-        __syncthreads();
+        if (NB == 2 || ODD) __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {
         step(t, IntTag<0>{});

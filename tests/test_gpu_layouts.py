@@ -164,9 +164,14 @@ def test_strided_c_abi_direct(vattn):
 # Grids that select each kernel shape: 16-wave blocks (256 rows) when there
 # are at least 256 of them, 8-wave blocks while 2x that reaches 256; below,
 # 64-row blocks: the split-key kernel while there are at most 256 of them,
-# else 4-wave blocks.
+# else 4-wave blocks.  The 16-wave kernel stores tiles two steps ahead and
+# synchronises after every odd step, so it also runs with 1, 2, 3 and 5 key
+# tiles (ragged and exact).
 WORKGROUP_SHAPES = [("split keys", 2, 1000), ("split keys ragged", 3, 333),
-                    ("4 waves", 20, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000)]
+                    ("4 waves", 20, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000),
+                    ("16 waves one tile", 300, 64), ("16 waves two tiles", 300, 128),
+                    ("16 waves three tiles ragged", 300, 150),
+                    ("16 waves five tiles ragged", 260, 300)]
 
 
 @pytest.mark.parametrize("label,h,n", WORKGROUP_SHAPES, ids=[s[0] for s in WORKGROUP_SHAPES])
