@@ -59,6 +59,38 @@ def read_traffic(workload_name: str):
         return None
 
 
+def read_counters(workload_name: str, precision: str):
+    """Matrix-core and vector-ALU figures of the attention kernel from the
+    committed rocprofv3 counter summary (profiles/attention_fwd_<workload>_mfma.txt,
+    one block of lines per precision), or None when there is none for this
+    precision or the kernel source changed since it was taken.
+
+    mfma_busy_pct: rocprofv3's MfmaUtil, matrix-core busy cycles over
+    GPU-active cycles times the SIMD count; valu_busy_pct: its VALUBusy;
+    mfma_f16_flops_per_launch: MfmaFlopsF16, the f16 MFMA work the hardware
+    executed (the AUTO/SPLIT corrections and the zero padding of head_dim < 64
+    included), next to the algorithmic 4*H*N^2*d."""
+    path = os.path.join(ROOT, "profiles", "attention_fwd_%s_mfma.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    out = {}
+    for key in ("mfma_busy_pct", "valu_busy_pct", "mfma_valu_coexec_pct",
+                "mfma_f16_flops_per_launch", "mfma_f16_flops_over_algorithmic"):
+        val = fields.get("%s.%s" % (precision, key))
+        if val is None:
+            return None
+        out[key] = float(val)
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
+
+
 def oracle_path(q, k, v, w, n_threads: int = 0, rows=None):
     """The whole path in the float64 oracle: rotary transform of Q and K (for
     the rotary workloads), then attention (all rows, or the listed rows)."""
@@ -104,9 +136,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads are independent; see the sharding plan in DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (heads are "
+              "independent, so several GPUs would each run the kernel on their own "
+              "share of the heads).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -204,6 +236,7 @@ def main():
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic},
         "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
+        "counters": read_counters(w.name, args.precision),
         "parity_sample": parity,
     }
     if args.cpu_seconds > 0:
