@@ -669,6 +669,64 @@ struct IntTag {
 // Waves per SIMD the register budget is sized for: 4 (128 VGPRs) for the
 // 8- and 16-wave workgroups; the 4-wave workgroups of small grids (one wave
 // per SIMD each, four tile loads per thread) get 2 (256 VGPRs).
+// Query fragment of this lane's row (B operand of S^T = K Q^T): columns
+// 32 st + 8 g4 ... + 7 of each k-step st, times log2(e), as f16 (RNE) in qh
+// and, with SPLIT, the remainder f16(x - f32(qh)) in ql.  Rows past the
+// head read 0.  ROPE turns each pair first (in f32): columns [c, c + 4) lie
+// on one side of half and of rope_dims (both multiples of 4), so they turn
+// with their partner columns.
+template <int D, bool SPLIT, int IO, typename T, bool ROPE>
+__device__ __forceinline__ void load_q_fragment(const T *__restrict__ qg, int row, int n_patches,
+                                                const Io &io, const Rope &rope, int g4,
+                                                half8_t (&qh)[Lds<D>::kKSteps],
+                                                half8_t (&ql)[Lds<D>::kKSteps]) {
+    __amdgpu_buffer_rsrc_t rq;
+    if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
+    typedef typename VecOf<T, 4>::type T4;
+    // Four query columns [c, c+4) of the row as f32 (0 past the head).
+    auto q4 = [&](int c) __attribute__((always_inline)) {
+        float4_t x = zero4();
+        if (row < n_patches) {
+            if constexpr (IO == kIoDense)
+                x = __builtin_convertvector(*reinterpret_cast<const T4 *>(qg + row * D + c), float4_t);
+            else
+                x = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io),
+                                            float4_t);
+        }
+        return x;
+    };
+    auto q4_rotated = [&](int c) __attribute__((always_inline)) {
+        float4_t x = q4(c);
+        if constexpr (ROPE) {
+            if (c < 2 * rope.half) {
+                const bool first = c < rope.half;
+                const int i = first ? c : c - rope.half;
+                const float4_t y = q4(first ? c + rope.half : c - rope.half);
+                float4_t cs[2];
+                load_cs4(rope_rsrc(rope, 0, n_patches), row, i, rope.half, cs);
+                x = rotate4(x, y, cs, first);
+            }
+        }
+        return x;
+    };
+#pragma unroll
+    for (int st = 0; st < Lds<D>::kKSteps; ++st) {
+        const int c = 32 * st + 8 * g4;
+        float4_t x0 = q4_rotated(c), x1 = q4_rotated(c + 4);
+        x0 *= kLog2e;
+        x1 *= kLog2e;
+        const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
+        qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        if constexpr (SPLIT) {
+            const half4_t e0 = cvt4(x0 - __builtin_convertvector(h0, float4_t));
+            const half4_t e1 = cvt4(x1 - __builtin_convertvector(h1, float4_t));
+            ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+        } else {
+            ql[st] = qh[st];
+        }
+    }
+}
+
 template <int WAVES>
 constexpr int kMinWavesPerSimd = WAVES == 4 ? 2 : 4;
 
@@ -728,53 +786,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
-    __amdgpu_buffer_rsrc_t rq;
-    if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
-    typedef typename VecOf<T, 4>::type T4;
-    // Four query columns [c, c+4) of this lane's row as f32 (0 past the head).
-    auto q4 = [&](int c) __attribute__((always_inline)) {
-        float4_t x = zero4();
-        if (row < n_patches) {
-            if constexpr (IO == kIoDense)
-                x = __builtin_convertvector(*reinterpret_cast<const T4 *>(qg + row * D + c), float4_t);
-            else
-                x = __builtin_convertvector(load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io),
-                                            float4_t);
-        }
-        return x;
-    };
-    // ROPE: columns [c, c+4) lie on one side of half and of rope_dims (both
-    // multiples of 4); rotate them with their partner columns.
-    auto q4_rotated = [&](int c) __attribute__((always_inline)) {
-        float4_t x = q4(c);
-        if constexpr (ROPE) {
-            if (c < 2 * rope.half) {
-                const bool first = c < rope.half;
-                const int i = first ? c : c - rope.half;
-                const float4_t y = q4(first ? c + rope.half : c - rope.half);
-                float4_t cs[2];
-                load_cs4(rope_rsrc(rope, 0, n_patches), row, i, rope.half, cs);
-                x = rotate4(x, y, cs, first);
-            }
-        }
-        return x;
-    };
-#pragma unroll
-    for (int st = 0; st < L::kKSteps; ++st) {
-        const int c = 32 * st + 8 * g4;
-        float4_t x0 = q4_rotated(c), x1 = q4_rotated(c + 4);
-        x0 *= kLog2e;
-        x1 *= kLog2e;
-        const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
-        qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        if constexpr (SPLIT) {
-            const half4_t e0 = cvt4(x0 - __builtin_convertvector(h0, float4_t));
-            const half4_t e1 = cvt4(x1 - __builtin_convertvector(h1, float4_t));
-            ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
-        } else {
-            ql[st] = qh[st];
-        }
-    }
+    load_q_fragment<D, SPLIT, IO, T, ROPE>(qg, row, n_patches, io, rope, g4, qh, ql);
 
     if constexpr (ROPE) {
         // Zero both cos/sin buffers first (a barrier orders these stores
@@ -946,35 +958,8 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // Query fragment, as in attention_fwd_kernel.
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
-    __amdgpu_buffer_rsrc_t rq;
-    if constexpr (IO != kIoDense) rq = tile_rsrc<D, IO>(qg, 0, n_patches, io);
+    load_q_fragment<D, SPLIT, IO, T, false>(qg, row, n_patches, io, no_rope, g4, qh, ql);
     typedef typename VecOf<T, 4>::type T4;
-#pragma unroll
-    for (int st = 0; st < L::kKSteps; ++st) {
-        float4_t x[2] = {zero4(), zero4()};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 32 * st + 8 * g4 + 4 * h;
-            if (row < n_patches) {
-                if constexpr (IO == kIoDense)
-                    x[h] = __builtin_convertvector(*reinterpret_cast<const T4 *>(qg + row * D + c),
-                                                   float4_t);
-                else
-                    x[h] = __builtin_convertvector(
-                        load_cols<T, 4, IO>(rq, row * io.stride_patch, c, io), float4_t);
-            }
-            x[h] *= kLog2e;
-        }
-        const half4_t h0 = cvt4(x[0]), h1 = cvt4(x[1]);
-        qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        if constexpr (SPLIT) {
-            const half4_t e0 = cvt4(x[0] - __builtin_convertvector(h0, float4_t));
-            const half4_t e1 = cvt4(x[1] - __builtin_convertvector(h1, float4_t));
-            ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
-        } else {
-            ql[st] = qh[st];
-        }
-    }
 
     store_tile<D, WAVES, SPLIT, T, false>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
     if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, TN, n_patches, map, regs, io);
