@@ -1034,38 +1034,52 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if (t + 1 < n_tiles) step(t + 1, IntTag<1>{});
     }
 
-    // Merge chunks 1..3 into chunk 0, one at a time, through the (now idle)
-    // K tile buffers: per row group 64 lanes x (16 o + m + l) floats.
+    // Merge chunks 1..3 into chunk 0 through the (now idle) K and V tile
+    // buffers: chunk c writes its state (per row group 64 lanes x (16 o + m
+    // + l) floats) to region c - 1, and after one barrier chunk 0 combines
+    // the four with the online-softmax rule.
     constexpr int kState = 4 * L::kDBlocks + 2;
-    float *xfer = reinterpret_cast<float *>(&kh_s[0][0][0]) + rgroup * 64 * kState;
-    static_assert(4 * 64 * kState * 4 <= (int)sizeof(kh_s), "merge buffer");
-#pragma unroll 1
-    for (int c = 1; c < kSplitChunks; ++c) {
-        if (chunk == c) {
+    constexpr int kRegion = 4 * 64 * kState;  // floats per chunk
+    static_assert(2 * kRegion * 4 <= (int)sizeof(kh_s) && kRegion * 4 <= (int)sizeof(vt_s),
+                  "merge buffers");
+    auto region = [&](int c) __attribute__((always_inline)) {
+        float *b = c < 3 ? reinterpret_cast<float *>(&kh_s[0][0][0]) + (c - 1) * kRegion
+                         : reinterpret_cast<float *>(&vt_s[0][0][0]);
+        return b + rgroup * 64 * kState;
+    };
+    if (chunk != 0) {
+        float *xfer = region(chunk);
+#pragma unroll
+        for (int db = 0; db < L::kDBlocks; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xfer[(4 * db + j) * 64 + lane] = o[db][j];
+        xfer[(4 * L::kDBlocks) * 64 + lane] = m_run;
+        xfer[(4 * L::kDBlocks + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (chunk == 0) {
+        float m_c[kSplitChunks];
+        m_c[0] = m_run;
+#pragma unroll
+        for (int c = 1; c < kSplitChunks; ++c) m_c[c] = region(c)[(4 * L::kDBlocks) * 64 + lane];
+        // m_new is finite: chunk 0 always holds key 0.  A chunk that never
+        // saw a key has m = -inf and weight 0.
+        const float m_new = fmaxf(fmaxf(m_c[0], m_c[1]), fmaxf(m_c[2], m_c[3]));
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int db = 0; db < L::kDBlocks; ++db) o[db] *= a0;
+        l_run *= a0;
+#pragma unroll
+        for (int c = 1; c < kSplitChunks; ++c) {
+            const float *xfer = region(c);
+            const float ac = __builtin_amdgcn_exp2f(m_c[c] - m_new);
 #pragma unroll
             for (int db = 0; db < L::kDBlocks; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) xfer[(4 * db + j) * 64 + lane] = o[db][j];
-            xfer[(4 * L::kDBlocks) * 64 + lane] = m_run;
-            xfer[(4 * L::kDBlocks + 1) * 64 + lane] = l_run;
+                for (int j = 0; j < 4; ++j) o[db][j] += xfer[(4 * db + j) * 64 + lane] * ac;
+            l_run += xfer[(4 * L::kDBlocks + 1) * 64 + lane] * ac;
         }
-        __syncthreads();
-        if (chunk == 0) {
-            const float m_c = xfer[(4 * L::kDBlocks) * 64 + lane];
-            const float l_c = xfer[(4 * L::kDBlocks + 1) * 64 + lane];
-            const float m_new = fmaxf(m_run, m_c);
-            // m_new is finite: chunk 0 always holds key 0.
-            const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
-            const float ac = __builtin_amdgcn_exp2f(m_c - m_new);
-#pragma unroll
-            for (int db = 0; db < L::kDBlocks; ++db)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[db][j] = o[db][j] * a0 + xfer[(4 * db + j) * 64 + lane] * ac;
-            l_run = l_run * a0 + l_c * ac;
-            m_run = m_new;
-        }
-        __syncthreads();
+        m_run = m_new;
     }
 
     if (chunk == 0) {
