@@ -779,15 +779,10 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const int n_tiles = (n_patches + kTileN - 1) / kTileN;
     const TileMap<D, WAVES> map(tid);
 
-    // Tile 0's loads go out first, so their latency overlaps the Q loads'.
+    // Tile 0's loads (and with ROPE its cos/sin rows) go out first, so their
+    // latency overlaps the Q loads'.
     TileRegs<D, WAVES, T> regs;
     load_tile<D, WAVES, IO>(kg, vg, 0, n_patches, map, regs, io);
-
-    // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
-    half8_t qh[L::kKSteps];
-    half8_t ql[L::kKSteps];
-    load_q_fragment<D, SPLIT, IO, T, ROPE>(qg, row, n_patches, io, rope, g4, qh, ql);
-
     if constexpr (ROPE) {
         // Zero both cos/sin buffers first (a barrier orders these stores
         // before every wave's copies), so no lane ever reads LDS the copies
@@ -797,6 +792,11 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         __syncthreads();
         copy_cs_rows<D, WAVES>(rope, 0, n_patches, cs_s[0], wave, lane);
     }
+
+    // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
+    half8_t qh[L::kKSteps];
+    half8_t ql[L::kKSteps];
+    load_q_fragment<D, SPLIT, IO, T, ROPE>(qg, row, n_patches, io, rope, g4, qh, ql);
     store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
     if (n_tiles > 1) {
         load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
