@@ -89,12 +89,23 @@ def _load():
 lib = _load()
 
 
+def _mode(precision: str | int) -> int:
+    """C precision code of "auto", "fast" or "split" (an int passes through:
+    the library rejects unknown codes with VATTN_ERR_ARG)."""
+    if isinstance(precision, str):
+        if precision not in PRECISION:
+            raise ValueError("precision must be one of %s, got %r"
+                             % (sorted(PRECISION), precision))
+        return PRECISION[precision]
+    return int(precision)
+
+
 def forward_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,
                 n_patches: int, head_dim: int, stream: int = 0,
                 precision: str | int = "auto") -> int:
     """Direct call of ``vattn_forward_precision`` with raw device pointers.
     Returns the status code (no exception)."""
-    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    mode = _mode(precision)
     return lib.vattn_forward_precision(q_ptr or None, k_ptr or None, v_ptr or None,
                                        out_ptr or None, int(n_heads), int(n_patches),
                                        int(head_dim), mode, stream or None)
@@ -105,7 +116,7 @@ def forward_strided_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_head
                         stream: int = 0, precision: str | int = "auto") -> int:
     """Direct call of ``vattn_forward_strided`` (strides in floats); returns
     the status code."""
-    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    mode = _mode(precision)
     return lib.vattn_forward_strided(q_ptr or None, k_ptr or None, v_ptr or None,
                                      out_ptr or None, int(n_heads), int(n_patches),
                                      int(head_dim), int(stride_head), int(stride_patch),
@@ -117,7 +128,7 @@ def forward_f16_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: i
                     stream: int = 0, precision: str | int = "auto") -> int:
     """Direct call of ``vattn_forward_f16`` (f16 tensors, strides in
     elements); returns the status code."""
-    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    mode = _mode(precision)
     return lib.vattn_forward_f16(q_ptr or None, k_ptr or None, v_ptr or None,
                                  out_ptr or None, int(n_heads), int(n_patches),
                                  int(head_dim), int(stride_head), int(stride_patch),
@@ -148,7 +159,7 @@ def forward_rope_raw(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: 
                      precision: str | int = "auto", f16: bool = False) -> int:
     """Direct call of ``vattn_forward_rope`` (or ``vattn_forward_rope_f16``);
     returns the status code."""
-    mode = PRECISION[precision] if isinstance(precision, str) else int(precision)
+    mode = _mode(precision)
     fn = lib.vattn_forward_rope_f16 if f16 else lib.vattn_forward_rope
     return fn(q_ptr or None, k_ptr or None, v_ptr or None, out_ptr or None, int(n_heads),
               int(n_patches), int(head_dim), int(stride_head), int(stride_patch),

@@ -149,6 +149,11 @@ def test_f16_reaches_launch_with_8_byte_alignment():
 def test_unknown_precision_mode():
     assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, 3) == vattn.VATTN_ERR_ARG
     assert vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, -1) == vattn.VATTN_ERR_ARG
+    # an unknown mode name is the binding's error, before any call
+    with pytest.raises(ValueError, match="precision"):
+        vattn.forward_raw(A, B, C, O, 4, 64, 64, 0, "fastest")
+    with pytest.raises(ValueError, match="precision"):
+        vattn.forward_rope_raw(A, B, C, O, 4, 64, 64, 64 * 64, 64, 64, T, 0, "exact")
 
 
 def test_inputs_may_alias_each_other():
