@@ -20,11 +20,13 @@
 //  * attention_fwd_split_kernel (small grids): 16 waves = 4 row groups x 4
 //    key chunks over 64 rows, each wave on a quarter of every tile's keys,
 //    the chunks' softmax states merged through LDS at the end.
-//  * Keys stream through LDS in tiles, double buffered.  Tile t+1 is loaded
-//    into registers with buffer loads (the hardware range check zero-fills
-//    rows past n_patches), converted to f16 with round-to-nearest-even and
-//    stored to the other LDS buffer while tile t is consumed; one barrier
-//    per tile.
+//  * Keys stream through LDS in tiles.  The next tile is loaded into
+//    registers with buffer loads (the hardware range check zero-fills rows
+//    past n_patches), converted to f16 with round-to-nearest-even and
+//    stored to a free LDS buffer while the current tile is consumed: two
+//    buffers and one barrier per tile, or (one 16-wave workgroup per CU,
+//    no rotary) four buffers, tiles stored two steps ahead and one barrier
+//    per two tiles.
 //  * Scores are produced transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_f16: the key fragment (A operand) comes from LDS,
 //    the query fragment (B operand) stays in registers.  In the 16x16
@@ -731,12 +733,13 @@ template <int WAVES>
 constexpr int kMinWavesPerSimd = WAVES == 4 ? 2 : 4;
 
 // ------------------------------------------------------------------ kernel
-// Per key tile t (one barrier each): tile t+1, already in registers, is
-// converted into LDS buffer (t+1)%2 and the loads of tile t+2 are issued;
-// then QK(t) from buffer t%2, softmax and PV(t).  A tile's HBM/L2 latency
-// hides behind a whole tile of compute.  Matrix and vector work overlap
-// across the waves each SIMD holds.  The loop is unrolled by two so LDS
-// buffer addresses are immediates.
+// Per key tile t: a later tile, already in registers, is converted into a
+// free LDS buffer and the loads of the tile after it are issued; then
+// QK(t), softmax and PV(t) from tile t's buffer (see `step` for the buffer
+// and barrier schedule).  A tile's HBM/L2 latency hides behind a whole tile
+// of compute.  Matrix and vector work overlap across the waves each SIMD
+// holds.  The loop is unrolled by two so that, with two buffers, LDS buffer
+// addresses are immediates.
 template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
 __global__ void __launch_bounds__(64 * WAVES, kMinWavesPerSimd<WAVES>)
 attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -900,7 +903,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
 // ------------------------------------------------------- split-key kernel
 // Small grids (at most one 64-row block per CU): 16 waves = 4 row groups x
 // 4 key chunks.  A workgroup owns 64 query rows; the keys stream through
-// LDS in tiles of 128 (double buffered, one barrier per tile, as above) and
+// LDS in tiles of 128 (two buffers, one barrier per tile) and
 // key chunk c of every tile - rows [32c, 32c + 32) - goes to the waves of
 // chunk c, so each wave keeps its own (m, l, o) over a quarter of the keys
 // (16 rows x 32 keys per tile: two 16-key blocks).  At the end the chunks'
