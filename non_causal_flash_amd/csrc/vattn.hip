@@ -108,8 +108,11 @@ hipError_t launch_split_keys(const T *q, const T *k, const T *v, T *out, const L
 
 // Workgroup size.  16 waves (256 query rows) share each K/V tile among the
 // most queries (least L2 traffic and conversion work per query) and run one
-// per CU: used when they still give every CU a workgroup.  Smaller grids
-// take 8 waves (two workgroups per CU) while those fill the CUs.  Below
+// per CU: used when they give at least three quarters of the CUs a
+// workgroup (below every CU, the busiest CUs run the same 256 rows as with
+// two 8-wave workgroups, and convert each K/V tile once instead of twice).
+// Smaller grids take 8 waves (two workgroups per CU) while those fill the
+// CUs.  Below
 // that, 64-row workgroups: the split-key kernel (16 waves, 4 per SIMD) while
 // there is at most one per CU, else 4-wave workgroups (two per CU).  The
 // rotary kernels skip the 8-wave and split-key steps.
@@ -118,7 +121,7 @@ hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchAr
     const int64_t wide_blocks =
         (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
                               vattn::Shape<D, 16>::kBlockM);
-    if (wide_blocks >= (ROPE ? kCusPerDevice / 2 : kCusPerDevice))
+    if (wide_blocks >= (ROPE ? kCusPerDevice / 2 : 3 * kCusPerDevice / 4))
         return launch<D, 16, SPLIT, IO, T, ROPE>(q, k, v, out, a);
     if constexpr (!ROPE) {
         if (2 * wide_blocks >= kCusPerDevice)

@@ -162,7 +162,7 @@ def test_strided_c_abi_direct(vattn):
 
 
 # Grids that select each kernel shape: 16-wave blocks (256 rows) when there
-# are at least 256 of them, 8-wave blocks while 2x that reaches 256; below,
+# are at least 192 of them, 8-wave blocks while 2x that reaches 256; below,
 # 64-row blocks: the split-key kernel while there are at most 256 of them,
 # else 4-wave blocks.  The 16-wave kernel stores tiles two steps ahead and
 # synchronises after every odd step, so it also runs with 1, 2, 3 and 5 key
