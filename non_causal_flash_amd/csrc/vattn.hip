@@ -112,10 +112,13 @@ hipError_t launch_split_keys(const T *q, const T *k, const T *v, T *out, const L
 // workgroup (below every CU, the busiest CUs run the same 256 rows as with
 // two 8-wave workgroups, and convert each K/V tile once instead of twice).
 // Smaller grids take 8 waves (two workgroups per CU) while those fill the
-// CUs.  Below
-// that, 64-row workgroups: the split-key kernel (16 waves, 4 per SIMD) while
-// there is at most one per CU, else 4-wave workgroups (two per CU).  The
-// rotary kernels skip the 8-wave and split-key steps.
+// CUs.  Below that, the split-key kernel over 64-row blocks (16 waves, 4 per
+// SIMD) while there is at most one such block per CU.  The grids left over
+// (more 64-row blocks than CUs, hence more than 64 wide blocks) run 8-wave
+// blocks on fewer CUs, which beats 64-row 4-wave blocks at one wave per SIMD
+// (3-6% on 20-40 heads of 600-1000 patches).  The rotary kernels skip the
+// 8-wave (it would spill) and split-key steps: 16 waves from half as many
+// blocks, 4-wave blocks below.
 template <int D, bool SPLIT, int IO, typename T, bool ROPE>
 hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     const int64_t wide_blocks =
@@ -131,8 +134,10 @@ hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchAr
                                   vattn::kSplitBlockM);
         if (small_blocks <= kCusPerDevice)
             return launch_split_keys<D, SPLIT, IO, T>(q, k, v, out, a);
+        return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+    } else {
+        return launch<D, 4, SPLIT, IO, T, ROPE>(q, k, v, out, a);
     }
-    return launch<D, 4, SPLIT, IO, T, ROPE>(q, k, v, out, a);
 }
 
 template <int D, int IO, typename T, bool ROPE>
