@@ -108,10 +108,11 @@ hipError_t launch_split_keys(const T *q, const T *k, const T *v, T *out, const L
 
 // Workgroup size.  16 waves (256 query rows) share each K/V tile among the
 // most queries (least L2 traffic and conversion work per query) and run one
-// per CU: used when they give at least three quarters of the CUs a
-// workgroup (below every CU, the busiest CUs run the same 256 rows as with
-// two 8-wave workgroups, and convert each K/V tile once instead of twice).
-// Smaller grids take 8 waves (two workgroups per CU) while those fill the
+// per CU: used when there are more than half as many of them as CUs.  Then
+// 8-wave blocks would put two workgroups on some CUs, whose 256 rows match
+// the 16-wave block's, but convert each K/V tile twice (AUTO 5-10% slower
+// at 144-204 blocks).  With at most half as many, 8-wave blocks (128 rows)
+// give each busy CU one workgroup: used while they number at least half the
 // CUs.  Below that, the split-key kernel over 64-row blocks (16 waves, 4 per
 // SIMD) while there is at most one such block per CU.  The grids left over
 // (more 64-row blocks than CUs, hence more than 64 wide blocks) run 8-wave
@@ -124,7 +125,7 @@ hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchAr
     const int64_t wide_blocks =
         (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
                               vattn::Shape<D, 16>::kBlockM);
-    if (wide_blocks >= (ROPE ? kCusPerDevice / 2 : 3 * kCusPerDevice / 4))
+    if (ROPE ? wide_blocks >= kCusPerDevice / 2 : wide_blocks > kCusPerDevice / 2)
         return launch<D, 16, SPLIT, IO, T, ROPE>(q, k, v, out, a);
     if constexpr (!ROPE) {
         if (2 * wide_blocks >= kCusPerDevice)

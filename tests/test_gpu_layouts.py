@@ -162,13 +162,14 @@ def test_strided_c_abi_direct(vattn):
 
 
 # Grids that select each kernel shape: 16-wave blocks (256 rows) when there
-# are at least 192 of them, 8-wave blocks while 2x that reaches 256; below,
+# are more than 128 of them, 8-wave blocks while 2x that reaches 256; below,
 # the split-key kernel while there are at most 256 64-row blocks, else
 # 8-wave blocks again (the rotary kernels use 4-wave blocks there).  The 16-wave kernel stores tiles two steps ahead and
 # synchronises after every odd step, so it also runs with 1, 2, 3 and 5 key
 # tiles (ragged and exact).
 WORKGROUP_SHAPES = [("split keys", 2, 1000), ("split keys ragged", 3, 333),
-                    ("8 waves below the CU count", 20, 1000), ("8 waves", 40, 1000), ("16 waves", 70, 1000),
+                    ("8 waves below the CU count", 20, 1000), ("8 waves", 32, 1000),
+                    ("16 waves above half the CUs", 40, 1000), ("16 waves", 70, 1000),
                     ("16 waves one tile", 300, 64), ("16 waves two tiles", 300, 128),
                     ("16 waves three tiles ragged", 300, 150),
                     ("16 waves five tiles ragged", 260, 300)]
