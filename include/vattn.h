@@ -59,28 +59,36 @@ typedef enum vattn_status {
 
 /* How the logits q.k are formed on the matrix cores.
  *
- * FAST:  one f16 x f16 product per logit (f32 accumulate).  The logit error
- *        grows with |q| |k| (about 2^-11 relative per product), which is
- *        fine while logits stay within a few tens.
+ * FAST:  one f16 x f16 product per logit (f32 accumulate).  The error of a
+ *        logit is at most 2^-10 sum_c |q_c k_c| (both operands rounded to
+ *        f16, relative error 2^-11 each): fine for unit-variance operands
+ *        scaled by 1/sqrt(head_dim); aligned operands with logits of more
+ *        than ~6 log2 units (~4 nats), or large operands whose products
+ *        cancel, miss the tolerance.
  * SPLIT: q = q_hi + q_lo and k = k_hi + k_lo with all four parts f16; the
  *        logit is q_hi.k_hi + q_lo.k_hi + q_hi.k_lo (three f16 products, f32
  *        accumulate), about 2^-21 relative per product, for every key.
  *        Three times the matrix-core work of FAST for the Q.K^T half.
- * AUTO:  SPLIT arithmetic where it can change the result, FAST elsewhere:
- *        the two correction products are added to a block of 16 keys of a
- *        16-query group only when some logit of the block lies within 16
- *        (log2 units, i.e. weight 2^-16) of its query's running maximum, and
- *        only for query groups whose running maximum exceeds 24 log2 units in
- *        magnitude (where the f16 logit error ~2^-11 |logit| becomes
- *        visible); on a query group's first key tile, before a running
- *        maximum exists, every block when some logit of the group exceeds
- *        24 in magnitude.  Same accuracy as SPLIT on sharp softmax rows at a
- *        fraction of its cost.  The decision uses the running maximum known
- *        when a block is processed: keys seen while a group's maximum was
- *        still below 24 in magnitude keep f16 logits (weights off by up to
- *        ~1%), which matters only if many of them end up close to a larger
- *        maximum found later.  Such orderings, and logits that are small only
- *        through cancellation of large |q| |k|, call for SPLIT.
+ * AUTO:  SPLIT arithmetic on every key that can carry weight, FAST on the
+ *        rest.  Keys are processed in tiles of 64 (128 for small grids);
+ *        a 16-key block of a 16-query group gets the two correction
+ *        products when some logit of the block lies within 20 log2 units
+ *        of its query's running maximum, and on the group's first tile
+ *        (before a running maximum exists).  The running maximum never
+ *        exceeds the final one, so every key that weighs at least 2^-20 of
+ *        the row maximum gets split-f16 logits, whatever the order of the
+ *        keys or the size of the operands.  A key further below weighs
+ *        less than 2^-20; there f16 P is a subnormal whose spacing (2^-24)
+ *        already exceeds what an f16 logit error of ~2^-11 of the logit
+ *        changes.  The decision itself uses the f16 logits, whose error is
+ *        below 2^-10 sum_c |q_c k_c|: for operands with sum_c |q_c k_c|
+ *        above ~4096 (log2 units) a key may be misplaced by more than four
+ *        log2 units relative to the window.  With a flat softmax every
+ *        block lies in the window and AUTO does SPLIT's work; with a sharp
+ *        one (large logits) most blocks fall below it and AUTO skips their
+ *        corrections.  Like every mode that rounds P and V to f16, the
+ *        result meets max-abs 2e-3 / relative L2 1e-3 as a statistical
+ *        property of the rounding, not as a worst case.
  */
 typedef enum vattn_precision {
     VATTN_PRECISION_AUTO = 0,
@@ -105,8 +113,9 @@ typedef enum vattn_precision {
  * stream  : hipStream_t to enqueue on (NULL = the default stream).
  *
  * Ownership: the caller owns all four buffers and keeps them alive until the
- * work on `stream` completes.  The library allocates nothing, keeps no state
- * between calls and is safe to call from several threads.
+ * work on `stream` completes.  The library allocates nothing and is safe to
+ * call from several threads; the only state it keeps between calls is each
+ * device's compute-unit count, read once (vattn_launch_shape).
  *
  * Errors: arguments are checked synchronously; on any error nothing is
  * enqueued and `out` is untouched.  On VATTN_OK the kernel is enqueued and
@@ -239,6 +248,33 @@ int vattn_forward_rope_f16(const void *q, const void *k, const void *v,
                            long long stride_head, long long stride_patch,
                            int rope_dims, const float *rope_table,
                            int precision, void *stream);
+
+/* Workgroup shapes of the attention kernel (values of vattn_launch_shape). */
+typedef enum vattn_shape {
+    VATTN_SHAPE_SPLIT_KEYS = 1,  /* 64 query rows, 16 waves = 4 row groups x 4
+                                    key chunks, states merged in LDS        */
+    VATTN_SHAPE_4_WAVES = 4,     /* 64 query rows (rotary kernels only)     */
+    VATTN_SHAPE_8_WAVES = 8,     /* 128 query rows                          */
+    VATTN_SHAPE_16_WAVES = 16    /* 256 query rows, one workgroup per CU    */
+} vattn_shape;
+
+/*
+ * vattn_launch_shape - the workgroup shape every attention entry point
+ * launches for n_heads x n_patches rows (rotary: rope != 0) on a device with
+ * cu_count compute units.  Host-only: touches no device.  The entry points
+ * call it with the CU count of the stream's device, queried once per device
+ * (hipDeviceAttributeMultiprocessorCount).  Rule, with W = n_heads *
+ * ceil(n_patches / 256) and S = n_heads * ceil(n_patches / 64):
+ *   16 waves  if 2W > cu_count (rotary: 2W >= cu_count);
+ *   rotary:   4 waves otherwise;
+ *   8 waves   if 2W >= cu_count;
+ *   split-key if S <= cu_count;
+ *   8 waves   otherwise.
+ * head_dim (1 ... 64) does not change the shape.  Returns a vattn_shape
+ * value, or -VATTN_ERR_SIZE when a size is < 1, head_dim > 64 or
+ * cu_count < 1.
+ */
+int vattn_launch_shape(int n_heads, int n_patches, int head_dim, int rope, int cu_count);
 
 /* Static, never-NULL description of a status code ("unknown status" for
  * values outside vattn_status). */

@@ -45,7 +45,14 @@ PRECISION = {"auto": 0, "fast": 1, "split": 2}
 # Symbols declared in include/vattn.h.
 EXPORTS = ("vattn_forward", "vattn_forward_precision", "vattn_forward_strided",
            "vattn_forward_f16", "vattn_rope_table", "vattn_forward_rope",
-           "vattn_forward_rope_f16", "vattn_status_string", "vattn_last_hip_error")
+           "vattn_forward_rope_f16", "vattn_status_string", "vattn_last_hip_error",
+           "vattn_launch_shape")
+
+# Workgroup shapes (vattn_shape in vattn.h).
+SHAPE_SPLIT_KEYS = 1
+SHAPE_4_WAVES = 4
+SHAPE_8_WAVES = 8
+SHAPE_16_WAVES = 16
 
 
 class VattnError(RuntimeError):
@@ -83,6 +90,8 @@ def _load():
     lib.vattn_status_string.restype = ctypes.c_char_p
     lib.vattn_last_hip_error.argtypes = []
     lib.vattn_last_hip_error.restype = ci
+    lib.vattn_launch_shape.argtypes = [ci, ci, ci, ci, ci]
+    lib.vattn_launch_shape.restype = ci
     return lib
 
 
@@ -184,6 +193,15 @@ def rope_table(n_positions: int, rope_dims: int, base: float = 10000.0, factors=
     if rc != VATTN_OK:
         raise VattnError(rc, lib)
     return table
+
+
+def launch_shape(n_heads: int, n_patches: int, head_dim: int, rope: bool = False,
+                 cu_count: int = 256) -> int:
+    """Workgroup shape ``vattn_launch_shape`` picks (host-only, no device):
+    SHAPE_SPLIT_KEYS, SHAPE_4_WAVES, SHAPE_8_WAVES or SHAPE_16_WAVES, or a
+    negative status for invalid sizes."""
+    return lib.vattn_launch_shape(int(n_heads), int(n_patches), int(head_dim), int(bool(rope)),
+                                  int(cu_count))
 
 
 def vattn_forward(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, n_heads: int,

@@ -119,6 +119,20 @@ constexpr int kTileN = 64;               // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 
+// How the logits q.k are formed (template parameter PREC).
+constexpr int kPrecFast = 0;   // one f16 x f16 product per logit
+constexpr int kPrecSplit = 1;  // split-f16 logits (q_hi k_hi + q_lo k_hi + q_hi k_lo) everywhere
+constexpr int kPrecAuto = 2;   // split-f16 logits on the key blocks whose f16 error can matter
+
+// AUTO policy, in log2 units (q is pre-multiplied by log2 e): a 16-key
+// block gets the split-f16 correction when some logit in it lies within
+// `window` of its query's running maximum (the running max never exceeds
+// the final one, so every key that can weigh 2^-window or more relative to
+// the row maximum is corrected).
+struct AutoPolicy {
+    float window;
+};
+
 // LDS tile layout (the same for every workgroup size).
 template <int D>
 struct Lds {
@@ -372,9 +386,10 @@ __device__ __forceinline__ void load_tile(const T *kg, const T *vg, int key0,
 }
 
 // Registers -> LDS, both row-major [key][dim] in f16 (RNE from f32); with
-// f32 inputs SPLIT also stores k_lo = f16(k - f32(f16(k))).  f16 inputs
-// are exact in f16 (no k_lo).
-template <int D, int WAVES, bool SPLIT, typename T, bool ROPE, int TN>
+// f32 inputs SPLIT and AUTO also store k_lo = f16(k - f32(f16(k))).  f16
+// inputs are exact in f16 (no k_lo).
+
+template <int D, int WAVES, int PREC, typename T, bool ROPE, int TN>
 __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, TN> &r,
                                            _Float16 (*kh)[Lds<D>::kKRow],
                                            _Float16 (*kl)[Lds<D>::kKRow],
@@ -384,13 +399,20 @@ __device__ __forceinline__ void store_tile(const TileRegs<D, WAVES, T, TN> &r,
     using S = Shape<D, WAVES, TN>;
     typedef typename VecOf<float, S::kKWidth>::type Vec;
     typedef typename VecOf<_Float16, S::kKWidth>::type Half;
+    constexpr bool KLO = PREC != kPrecFast;
     // f32 K (or rotated K) -> f16 hi, and with SPLIT lo = f16(k - f32(hi)).
     auto put_k = [&](int row, int col, const Vec &x) __attribute__((always_inline)) {
         const Half hi = __builtin_convertvector(x, Half);
         *reinterpret_cast<Half *>(&kh[row][col]) = hi;
-        if constexpr (SPLIT)
-            *reinterpret_cast<Half *>(&kl[row][col]) =
-                __builtin_convertvector(x - __builtin_convertvector(hi, Vec), Half);
+        if constexpr (KLO) {
+            // x - f32(hi) is exact in f32; fma(hi, -1, x) lets the f16
+            // operand enter without a separate conversion (v_fma_mix_f32).
+            Vec lo;
+#pragma unroll
+            for (int j = 0; j < S::kKWidth; ++j)
+                lo[j] = __builtin_fmaf((float)hi[j], -1.0f, x[j]);
+            *reinterpret_cast<Half *>(&kl[row][col]) = __builtin_convertvector(lo, Half);
+        }
     };
     // ROPE: this lane's columns [col, col + width) are first halves
     // (col < half), second halves (col < 2 half) or unrotated; the other
@@ -443,27 +465,9 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// S'^T = K Q^T + C for one 64-key tile and the wave's 16 queries.  `c0`
-// starts every key block's accumulator at -m_ref, so the matrix core already
-// subtracts the running max from each logit.
-//
-// SPLIT adds q_lo.k_hi + q_hi.k_lo to a 16-key block after the q_hi.k_hi
-// pass, but only where it can matter: when some lane's scores in the block
-// lie above -lo_window relative to m_ref (lo_window = +inf: every block,
-// -inf: none).  A key whose f16 logit sits more than lo_window below the
-// running max has weight below 2^-lo_window, so the ~2^-11 relative error
-// its q_hi.k_hi logit carries is negligible in the output.  On a wave's
-// first tile there is no running max yet (m_ref = 0, s holds the logits):
-// every block is corrected when some logit of the wave exceeds lo_gate in
-// magnitude (the size below which f16 logits are accurate enough), none
-// otherwise.  KLO = false
-// (f16 inputs: k is exact in f16) drops the q_hi.k_lo product.
-//
-// bmax[kb] receives the lane's maximum over block kb before any correction
-// (the softmax reuses it: a correction moves a score by ~2^-11 of its size,
-// which matters for no reference-max or dead-block decision, and blocks in
-// the correction window are never dead).
-// q_lo.k_hi (+ q_hi.k_lo) added to the scores of 16-key block kb.
+// q_lo.k_hi (+ q_hi.k_lo) added to the scores of 16-key block kb, in the
+// block's accumulator.  KLO = false (f16 inputs: k is exact in f16) drops
+// the q_hi.k_lo product.
 template <int D, bool KLO, int KB>
 __device__ __forceinline__ void qk_correct(const _Float16 (*kh)[Lds<D>::kKRow],
                                            const _Float16 (*kl)[Lds<D>::kKRow],
@@ -482,25 +486,40 @@ __device__ __forceinline__ void qk_correct(const _Float16 (*kh)[Lds<D>::kKRow],
     }
 }
 
-// In-lane maximum magnitude of the scores.
+// In-lane maxima of the scores: per 16-key block (bmax), per 32-key half
+// (mxh) and over the tile (mx).
 template <int KB>
-__device__ __forceinline__ float lane_abs_max(const float4_t (&s)[KB]) {
-    float a = 0.f;
+__device__ __forceinline__ void tile_maxima(const float4_t (&s)[KB], float (&bmax)[KB],
+                                            float (&mxh)[KB / 2], float &mx) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(s[kb][0]), fabsf(s[kb][1])),
-                           fmaxf(fabsf(s[kb][2]), fabsf(s[kb][3]))));
-    return a;
+        bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
+#pragma unroll
+    for (int ks = 0; ks < KB / 2; ++ks) mxh[ks] = fmaxf(bmax[2 * ks], bmax[2 * ks + 1]);
+    mx = mxh[0];
+#pragma unroll
+    for (int ks = 1; ks < KB / 2; ++ks) mx = fmaxf(mx, mxh[ks]);
 }
 
-template <int D, bool SPLIT, bool KLO, int KB = 4>
-__device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
-                                        const _Float16 (*kl)[Lds<D>::kKRow],
-                                        const half8_t (&qh)[Lds<D>::kKSteps],
-                                        const half8_t (&ql)[Lds<D>::kKSteps], float4_t c0,
-                                        float4_t (&s)[KB], float (&bmax)[KB], int l16, int g4,
-                                        float lo_window, bool first = false,
-                                        float lo_gate = 0.f) {
+// S'^T = K Q^T + C for one tile of 16*KB keys and the wave's 16 queries.
+// `c0` starts every key block's accumulator at -m_ref, so the matrix core
+// already subtracts the running max from each logit.  Keys at or past
+// key_lim (the ragged last tile) are set to -inf before anything looks at
+// the scores.  bmax, mxh and mx receive the lane's maxima (tile_maxima)
+// before any correction: a correction moves a score by ~2^-11 of its size,
+// which matters for no reference-max, window or dead-half decision.
+//
+// Returns the wave-uniform mask of the blocks that need the split-f16
+// correction (apply_corrections): none for FAST, all for SPLIT, and for
+// AUTO the blocks with a logit inside the window of the running max
+// (AutoPolicy).  On a wave's first tile (`first`) there is no running max:
+// every block counts as inside the window.
+template <int D, int PREC, int KB = 4>
+__device__ __forceinline__ unsigned qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
+                                            const half8_t (&qh)[Lds<D>::kKSteps], float4_t c0,
+                                            float4_t (&s)[KB], float (&bmax)[KB],
+                                            float (&mxh)[KB / 2], float &mx, int l16, int g4,
+                                            int key_lim, const AutoPolicy &pol, bool first) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -510,28 +529,47 @@ __device__ __forceinline__ void qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
             s[kb] = mfma16(a, qh[st], st == 0 ? c0 : s[kb]);
         }
     }
+    if (key_lim < 16 * KB) {  // wave-uniform: only the ragged last tile
+        // Key 16 kb + 4 g4 + i of the tile is past the end when 16 kb + i >=
+        // key_lim - 4 g4 (compile-time constants against one lane value).
+        const int lim = key_lim - 4 * g4;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
-    auto correct = [&](int kb) __attribute__((always_inline)) {
-        qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
-    };
-    // lo_window and first are wave-uniform: skip the block tests when no
-    // block can pass, and test magnitudes only on the first tile.
-    if (SPLIT && lo_window != -__builtin_inff()) {
-        if (first) {
-            // No running max yet: if any logit of the wave exceeds lo_gate
-            // in magnitude, the tile's keys near each query's maximum are
-            // not known before the cross-lane max, so correct every block.
-            if (__ballot(lane_abs_max(s) > lo_gate)) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) correct(kb);
-            }
-        } else {
+            for (int i = 0; i < 4; ++i)
+                if (16 * kb + i >= lim) s[kb][i] = -__builtin_inff();
+    }
+    tile_maxima(s, bmax, mxh, mx);
+    constexpr unsigned kAll = (1u << KB) - 1;
+    if constexpr (PREC == kPrecSplit) {
+        return kAll;
+    } else if constexpr (PREC == kPrecAuto) {
+        if (first) return kAll;
+        unsigned mask = 0;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                if (__ballot(bmax[kb] > -lo_window)) correct(kb);
-        }
+        for (int kb = 0; kb < KB; ++kb)
+            if (__ballot(bmax[kb] > -pol.window)) mask |= 1u << kb;
+        return mask;
+    } else {
+        return 0;
+    }
+}
+
+// q_lo.k_hi (+ q_hi.k_lo) added to the blocks of `mask` (SPLIT: to every
+// block, unconditionally).
+template <int D, int PREC, bool KLO, int KB>
+__device__ __forceinline__ void apply_corrections(const _Float16 (*kh)[Lds<D>::kKRow],
+                                                  const _Float16 (*kl)[Lds<D>::kKRow],
+                                                  const half8_t (&qh)[Lds<D>::kKSteps],
+                                                  const half8_t (&ql)[Lds<D>::kKSteps],
+                                                  float4_t (&s)[KB], unsigned mask, int l16,
+                                                  int g4) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        if constexpr (PREC == kPrecSplit)
+            qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
+        else if (mask & (1u << kb))
+            qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
     }
 }
 
@@ -598,50 +636,33 @@ __device__ __forceinline__ void exp_pv_live(const float4_t (&s)[KB], const float
 
 // Online softmax and P.V for one tile whose scores s hold s_true - m_run
 // (the QK accumulator started at c0 = -m_run; before the first tile
-// m_run = -inf and c0 = 0).  The running max is raised only when the tile's
+// m_run = -inf and c0 = 0; keys past n_patches already hold -inf).  The
+// running max is raised only when the tile's
 // max exceeds it by more than kRescaleSlack: then o and l are scaled by
 // 2^(m_old - m_new), s is rebased and c0 follows.  That branch is
 // wave-uniform; it carries its own copy of the exponentials and the P.V
 // product, so the common path joins the rare one only after values both
 // sides compute afresh (no register copies).
-// RECOMPUTE: take the blocks' maxima afresh from s instead of keeping
-// qk_tile's across the corrections (fewer live registers, for kernels that
-// are short of them).
+// bmax, mxh, mx: qk_tile's maxima (tile_maxima).  RECOMPUTE: take them
+// afresh from s instead of keeping qk_tile's across the corrections (fewer
+// live registers, for kernels that are short of them).
 // The wave runs this at raised issue priority: its exponentials stand
 // between its scores and its P.V products, and the waves still issuing
 // score MFMAs lose little by yielding to it.  (Measured: 8-wave d = 32
 // blocks two to a CU +5%, the other shapes equal.)
-template <int D, bool MASK, int KB = 4, bool RECOMPUTE = false>
-__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)[KB], float4_t &c0,
+template <int D, int KB = 4, bool RECOMPUTE = false>
+__device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)[KB],
+                                                float (&mxh)[KB / 2], float mx, float4_t &c0,
                                                 float &m_run, float &l_run,
                                                 float4_t (&o)[Lds<D>::kDBlocks],
                                                 const _Float16 (*vt)[Lds<D>::kKRow],
-                                                int key_lim, int l16, int g4) {
+                                                int l16, int g4) {
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (MASK) {  // ragged last tile: keys past n_patches drop out
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (16 * kb + 4 * g4 + i >= key_lim) s[kb][i] = -__builtin_inff();
-    }
-    if constexpr (MASK || RECOMPUTE) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            bmax[kb] = fmaxf(fmaxf(fmaxf(s[kb][0], s[kb][1]), s[kb][2]), s[kb][3]);
-    }
-    // In-lane maxima of each 32-key half (from the blocks' maxima of
-    // qk_tile) and over the tile.
-    float mxh[KB / 2];
-#pragma unroll
-    for (int ks = 0; ks < KB / 2; ++ks) mxh[ks] = fmaxf(bmax[2 * ks], bmax[2 * ks + 1]);
-    float mx = mxh[0];
-#pragma unroll
-    for (int ks = 1; ks < KB / 2; ++ks) mx = fmaxf(mx, mxh[ks]);
+    if constexpr (RECOMPUTE) tile_maxima(s, bmax, mxh, mx);
     const float m_ref = -c0[0];
     // Some lane's own scores exceed the slack: only then is the query's
     // tile max (across its 4 lane groups) needed.
-    if (__ballot(mx + m_ref > m_run + kRescaleSlack)) {
+    if (__ballot(mx - c0[0] > m_run + kRescaleSlack)) {
         const float tile_max = max_lane_groups(mx) + m_ref;
         const bool raise = tile_max > m_run + kRescaleSlack;
         const float m_new = raise ? tile_max : m_run;
@@ -677,7 +698,7 @@ struct IntTag {
 // head read 0.  ROPE turns each pair first (in f32): columns [c, c + 4) lie
 // on one side of half and of rope_dims (both multiples of 4), so they turn
 // with their partner columns.
-template <int D, bool SPLIT, int IO, typename T, bool ROPE>
+template <int D, int PREC, int IO, typename T, bool ROPE>
 __device__ __forceinline__ void load_q_fragment(const T *__restrict__ qg, int row, int n_patches,
                                                 const Io &io, const Rope &rope, int g4,
                                                 half8_t (&qh)[Lds<D>::kKSteps],
@@ -719,12 +740,55 @@ __device__ __forceinline__ void load_q_fragment(const T *__restrict__ qg, int ro
         x1 *= kLog2e;
         const half4_t h0 = cvt4(x0), h1 = cvt4(x1);
         qh[st] = (half8_t){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        if constexpr (SPLIT) {
+        if constexpr (PREC != kPrecFast) {
             const half4_t e0 = cvt4(x0 - __builtin_convertvector(h0, float4_t));
             const half4_t e1 = cvt4(x1 - __builtin_convertvector(h1, float4_t));
             ql[st] = (half8_t){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
         } else {
             ql[st] = qh[st];
+        }
+    }
+}
+
+// This lane's index in its wave, computed afresh with v_mbcnt: values
+// derived from it after the tile loop are not kept alive (or spilled)
+// across the loop.
+__device__ __forceinline__ int fresh_lane_id() {
+    int id;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(id));
+    return id;
+}
+
+// Epilogue: out = O / l for the wave's 16 rows starting at row0 (inside the
+// head: rows below n_patches; in the strided modes columns below
+// head_dim).  O^T block db holds dims 16 db + 4 g4 .. + 3 of query l16.
+template <int D, int IO, typename T>
+__device__ __forceinline__ void store_rows(T *__restrict__ og, const float4_t (&o)[Lds<D>::kDBlocks],
+                                           float l_run, int row0, int n_patches, const Io &io) {
+    const float inv = 1.0f / sum_lane_groups(l_run);
+    const int lane = fresh_lane_id();
+    const int row = row0 + (lane & 15);
+    const int g4 = lane >> 4;
+    if (row >= n_patches) return;
+    typedef typename VecOf<T, 4>::type T4;
+    if constexpr (IO == kIoDense) {
+#pragma unroll
+        for (int db = 0; db < Lds<D>::kDBlocks; ++db)
+            *reinterpret_cast<T4 *>(og + row * D + 16 * db + 4 * g4) =
+                __builtin_convertvector(o[db] * inv, T4);
+    } else {
+        T *orow = og + (size_t)row * io.stride_patch;
+#pragma unroll
+        for (int db = 0; db < Lds<D>::kDBlocks; ++db) {
+            const int c = 16 * db + 4 * g4;
+            const T4 y = __builtin_convertvector(o[db] * inv, T4);
+            if constexpr (IO == kIoVec4) {
+                if (c < io.head_dim) *reinterpret_cast<T4 *>(orow + c) = y;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (c + j < io.head_dim) orow[c + j] = y[j];
+            }
         }
     }
 }
@@ -740,17 +804,18 @@ constexpr int kMinWavesPerSimd = WAVES == 4 ? 2 : 4;
 // of compute.  Matrix and vector work overlap across the waves each SIMD
 // holds.  The loop is unrolled by two so that, with two buffers, LDS buffer
 // addresses are immediates.
-template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
+template <int D, int WAVES, int PREC, int IO, typename T, bool ROPE>
 __global__ void __launch_bounds__(64 * WAVES, kMinWavesPerSimd<WAVES>)
 attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      const T *__restrict__ v, T *__restrict__ out,
-                     int n_patches, int q_blocks, int total_blocks, float lo_window,
-                     float lo_gate, Io io, Rope rope) {
+                     int n_patches, int q_blocks, int total_blocks, AutoPolicy pol, Io io,
+                     Rope rope) {
     using L = Lds<D>;
     using S = Shape<D, WAVES>;
+    using M = TileMap<D, WAVES>;
     // k_lo tiles: f32 K, or rotated K (f16 inputs are exact in f16 only
     // before the rotation).
-    constexpr bool KLO = SPLIT && (sizeof(T) == 4 || ROPE);
+    constexpr bool KLO = PREC != kPrecFast && (sizeof(T) == 4 || ROPE);
     // LDS buffers of K/V tiles.  One workgroup per CU (16 waves, no rotary
     // tables) has room for four: tiles are stored two steps ahead and one
     // barrier follows every second step.  Otherwise two: one step ahead, a
@@ -774,13 +839,13 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     T *__restrict__ og = out + base;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l16 = lane & 15;  // query column inside the wave's 16 rows
     const int g4 = lane >> 4;   // lane group 0..3
     const int row = qblk * S::kBlockM + wave * kRowsPerWave + l16;
     const int n_tiles = (n_patches + kTileN - 1) / kTileN;
-    const TileMap<D, WAVES> map(tid);
+    const M map(tid);
 
     // Tile 0's loads (and with ROPE its cos/sin rows) go out first, so their
     // latency overlaps the Q loads'.
@@ -799,16 +864,16 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // Query fragment (B operand of S^T = K Q^T), pre-multiplied by log2(e).
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
-    load_q_fragment<D, SPLIT, IO, T, ROPE>(qg, row, n_patches, io, rope, g4, qh, ql);
-    store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
+    load_q_fragment<D, PREC, IO, T, ROPE>(qg, row, n_patches, io, rope, g4, qh, ql);
+    store_tile<D, WAVES, PREC, T, ROPE>(regs, kh_s[0], kl_s[0], vt_s[0], map, rope, cs_s[0], lane);
     if (n_tiles > 1) {
         load_tile<D, WAVES, IO>(kg, vg, kTileN, n_patches, map, regs, io);
         if constexpr (ROPE) copy_cs_rows<D, WAVES>(rope, kTileN, n_patches, cs_s[1], wave, lane);
     }
     if constexpr (AHEAD == 2) {
         if (n_tiles > 1) {
-            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[1], kl_s[KLO ? 1 : 0], vt_s[1], map,
-                                                 rope, cs_s[0], lane);
+            store_tile<D, WAVES, PREC, T, ROPE>(regs, kh_s[1], kl_s[KLO ? 1 : 0], vt_s[1], map,
+                                                rope, cs_s[0], lane);
             if (n_tiles > 2) load_tile<D, WAVES, IO>(kg, vg, 2 * kTileN, n_patches, map, regs, io);
         }
     }
@@ -825,17 +890,17 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // previous step) goes into LDS buffer (t + AHEAD) % NB, then the loads of
     // the tile after it are issued: they drain while this tile is computed,
     // and the stores have landed long before the next barrier.  The buffer a
-    // store overwrites was read AHEAD steps earlier, before the last barrier
-    // every wave has passed; a tile stored in step t is read in step
-    // t + AHEAD, after the barrier that ends the group of AHEAD steps
-    // holding step t.
+    // store overwrites (tile data and bound-test bytes) was read AHEAD steps
+    // earlier, before the last barrier every wave has passed; a tile stored
+    // in step t is read in step t + AHEAD, after the barrier that ends the
+    // group of AHEAD steps holding step t.
     auto step = [&](int t, auto odd_tag) __attribute__((always_inline)) {
         constexpr int ODD = decltype(odd_tag)::value;
         const int rb = NB == 2 ? ODD : (t & 3);          // buffer of tile t
         const int wb = NB == 2 ? ODD ^ 1 : ((t + 2) & 3);  // buffer of tile t + AHEAD
         if (t + AHEAD < n_tiles) {
-            store_tile<D, WAVES, SPLIT, T, ROPE>(regs, kh_s[wb], kl_s[KLO ? wb : 0], vt_s[wb], map,
-                                                 rope, cs_s[ROPE ? wb : 0], lane);
+            store_tile<D, WAVES, PREC, T, ROPE>(regs, kh_s[wb], kl_s[KLO ? wb : 0], vt_s[wb], map,
+                                                rope, cs_s[ROPE ? wb : 0], lane);
             if (t + AHEAD + 1 < n_tiles) {
                 load_tile<D, WAVES, IO>(kg, vg, (t + AHEAD + 1) * kTileN, n_patches, map, regs,
                                         io);
@@ -846,25 +911,12 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
             }
         }
         float4_t s[4];
-        float bmax[4];
-        // Correction window of the SPLIT kernel: on the first tile (no
-        // running max yet) the blocks with logits above lo_gate in magnitude;
-        // later, lo_window for waves whose running max has magnitude above
-        // lo_gate (large logits), none otherwise.
-        float win = __builtin_inff();
-        const bool first = m_run == -__builtin_inff();
-        if constexpr (SPLIT) {
-            if (!first) win = __ballot(fabsf(m_run) > lo_gate) ? lo_window : -__builtin_inff();
-        }
-        qk_tile<D, SPLIT, KLO>(kh_s[rb], kl_s[KLO ? rb : 0], qh, ql, c0, s, bmax, l16, g4, win,
-                               first, lo_gate);
-        const int key_lim = n_patches - t * kTileN;
-        if (key_lim < kTileN)
-            softmax_pv_tile<D, true, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[rb], key_lim, l16,
-                                              g4);
-        else
-            softmax_pv_tile<D, false, 4, ROPE>(s, bmax, c0, m_run, l_run, o, vt_s[rb], key_lim,
-                                               l16, g4);
+        float bmax[4], mxh[2], mx;
+        const unsigned fix = qk_tile<D, PREC>(kh_s[rb], qh, c0, s, bmax, mxh, mx, l16, g4,
+                                              n_patches - t * kTileN, pol, t == 0);
+        if constexpr (PREC != kPrecFast)
+            apply_corrections<D, PREC, KLO>(kh_s[rb], kl_s[KLO ? rb : 0], qh, ql, s, fix, l16, g4);
+        softmax_pv_tile<D, 4, ROPE>(s, bmax, mxh, mx, c0, m_run, l_run, o, vt_s[rb], l16, g4);
         if (NB == 2 || ODD) __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {
@@ -872,32 +924,7 @@ attention_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if (t + 1 < n_tiles) step(t + 1, IntTag<1>{});
     }
 
-    // Epilogue: out = O / l for rows inside the head (and, in the strided
-    // modes, columns below head_dim).
-    const float inv = 1.0f / sum_lane_groups(l_run);
-    if (row < n_patches) {
-        typedef typename VecOf<T, 4>::type T4;
-        if constexpr (IO == kIoDense) {
-#pragma unroll
-            for (int db = 0; db < L::kDBlocks; ++db)
-                *reinterpret_cast<T4 *>(og + row * D + 16 * db + 4 * g4) =
-                    __builtin_convertvector(o[db] * inv, T4);
-        } else {
-            T *orow = og + (size_t)row * io.stride_patch;
-#pragma unroll
-            for (int db = 0; db < L::kDBlocks; ++db) {
-                const int c = 16 * db + 4 * g4;
-                const T4 y = __builtin_convertvector(o[db] * inv, T4);
-                if constexpr (IO == kIoVec4) {
-                    if (c < io.head_dim) *reinterpret_cast<T4 *>(orow + c) = y;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (c + j < io.head_dim) orow[c + j] = y[j];
-                }
-            }
-        }
-    }
+    store_rows<D, IO, T>(og, o, l_run, qblk * S::kBlockM + wave * kRowsPerWave, n_patches, io);
 }
 
 // ------------------------------------------------------- split-key kernel
@@ -914,24 +941,23 @@ constexpr int kSplitChunks = 4;
 constexpr int kSplitTileN = 32 * kSplitChunks;  // keys per LDS tile
 constexpr int kSplitBlockM = 64;                // query rows per workgroup
 
-template <int D, bool SPLIT, int IO, typename T>
+template <int D, int PREC, int IO, typename T>
 __global__ void __launch_bounds__(1024, 4)
 attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
                            const T *__restrict__ v, T *__restrict__ out, int n_patches,
-                           int q_blocks, int total_blocks, float lo_window, float lo_gate,
-                           Io io) {
+                           int q_blocks, int total_blocks, AutoPolicy pol, Io io) {
     using L = Lds<D>;
     constexpr int WAVES = 16;
     constexpr int TN = kSplitTileN;
-    constexpr bool KLO = SPLIT && sizeof(T) == 4;
+    using M = TileMap<D, WAVES, TN>;
+    constexpr bool KLO = PREC != kPrecFast && sizeof(T) == 4;
     __shared__ __attribute__((aligned(16))) _Float16 kh_s[2][TN][L::kKRow];
     __shared__ __attribute__((aligned(16))) _Float16 vt_s[2][TN][L::kKRow];
     __shared__ __attribute__((aligned(16)))
     _Float16 kl_s[KLO ? 2 : 1][KLO ? TN : 1][L::kKRow];
-    // SPLIT/AUTO gate of every wave, [step parity][row group][key chunk]: a
-    // chunk sees only a quarter of the keys, so whether a row group's logits
-    // are large enough for corrections is decided from all four chunks.
-    __shared__ __attribute__((aligned(16))) int gate_s[2][4][kSplitChunks];
+    // AUTO: a chunk decides its corrections from its own running max,
+    // which never exceeds its row group's, so its window test keeps every
+    // key within the window of the group's maximum.
 
     const int logical = xcd_remap(blockIdx.x, total_blocks);
     const int head = logical / q_blocks;
@@ -944,7 +970,7 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     T *__restrict__ og = out + base;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
@@ -952,7 +978,7 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const int chunk = wave & 3;    // 32-key chunk of every tile
     const int row = qblk * kSplitBlockM + rgroup * kRowsPerWave + l16;
     const int n_tiles = (n_patches + TN - 1) / TN;
-    const TileMap<D, WAVES, TN> map(tid);
+    const M map(tid);
 
     const Rope no_rope{nullptr, 0};
     TileRegs<D, WAVES, T, TN> regs;
@@ -961,10 +987,9 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     // Query fragment, as in attention_fwd_kernel.
     half8_t qh[L::kKSteps];
     half8_t ql[L::kKSteps];
-    load_q_fragment<D, SPLIT, IO, T, false>(qg, row, n_patches, io, no_rope, g4, qh, ql);
-    typedef typename VecOf<T, 4>::type T4;
-
-    store_tile<D, WAVES, SPLIT, T, false>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr, lane);
+    load_q_fragment<D, PREC, IO, T, false>(qg, row, n_patches, io, no_rope, g4, qh, ql);
+    store_tile<D, WAVES, PREC, T, false>(regs, kh_s[0], kl_s[0], vt_s[0], map, no_rope, nullptr,
+                                         lane);
     if (n_tiles > 1) load_tile<D, WAVES, IO>(kg, vg, TN, n_patches, map, regs, io);
     __syncthreads();
 
@@ -979,56 +1004,24 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
     auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
         constexpr int BUF = decltype(buf_tag)::value;
         if (t + 1 < n_tiles) {
-            store_tile<D, WAVES, SPLIT, T, false>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
-                                           vt_s[BUF ^ 1], map, no_rope, nullptr, lane);
+            store_tile<D, WAVES, PREC, T, false>(regs, kh_s[BUF ^ 1], kl_s[KLO ? (BUF ^ 1) : 0],
+                                                 vt_s[BUF ^ 1], map, no_rope, nullptr, lane);
             if (t + 2 < n_tiles)
                 load_tile<D, WAVES, IO>(kg, vg, (t + 2) * TN, n_patches, map, regs, io);
         }
         const int key_lim = n_patches - t * TN - key_off;
-        const bool live = key_lim > 0;  // wave-uniform: a chunk past the last key does nothing
-        const _Float16(*kh)[L::kKRow] = kh_s[BUF] + key_off;
-        const _Float16(*kl)[L::kKRow] = kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0);
-        float4_t s[2];
-        float bmax[2];
-        // Row-group gate of the SPLIT kernel, shared by its 4 key chunks.
-        // First tile: every block is corrected if some logit of the row
-        // group exceeds lo_gate in magnitude (exchanged behind one extra
-        // barrier).  Later tiles: the lo_window test, relative to the
-        // chunk's own running max (never above the row group's, so the test
-        // includes every key within lo_window of the true max), in row
-        // groups where some chunk's running max exceeds lo_gate in
-        // magnitude (flags written at the end of the previous step).
-        if constexpr (SPLIT) {
-            if (t == 0) {
-                if (live) qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4,
-                                                    -__builtin_inff());
-                const bool big = live && __ballot(lane_abs_max(s) > lo_gate);
-                if (lane == 0) gate_s[1][rgroup][chunk] = big;
-                __syncthreads();
-                const int4 f = *reinterpret_cast<const int4 *>(&gate_s[1][rgroup][0]);
-                if (live && (f.x | f.y | f.z | f.w)) {
-                    qk_correct<D, KLO, 2>(kh, kl, qh, ql, s, 0, l16, g4);
-                    qk_correct<D, KLO, 2>(kh, kl, qh, ql, s, 1, l16, g4);
-                }
-            } else if (live) {
-                const int4 f = *reinterpret_cast<const int4 *>(&gate_s[(t - 1) & 1][rgroup][0]);
-                const float win = (f.x | f.y | f.z | f.w) ? lo_window : -__builtin_inff();
-                qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4, win);
-            }
-        } else if (live) {
-            qk_tile<D, SPLIT, KLO, 2>(kh, kl, qh, ql, c0, s, bmax, l16, g4, -__builtin_inff());
-        }
-        if (live) {
-            if (key_lim < 32)
-                softmax_pv_tile<D, true, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
-                                            l16, g4);
-            else
-                softmax_pv_tile<D, false, 2>(s, bmax, c0, m_run, l_run, o, vt_s[BUF] + key_off, key_lim,
-                                             l16, g4);
-        }
-        if constexpr (SPLIT) {
-            if (lane == 0)
-                gate_s[t & 1][rgroup][chunk] = m_run != -__builtin_inff() && fabsf(m_run) > lo_gate;
+        // wave-uniform: a chunk past the last key does nothing
+        if (key_lim > 0) {
+            float4_t s[2];
+            float bmax[2], mxh[1], mx;
+            const unsigned fix = qk_tile<D, PREC, 2>(kh_s[BUF] + key_off, qh, c0, s, bmax, mxh,
+                                                     mx, l16, g4, key_lim, pol, t == 0);
+            if constexpr (PREC != kPrecFast)
+                apply_corrections<D, PREC, KLO>(kh_s[BUF] + key_off,
+                                          kl_s[KLO ? BUF : 0] + (KLO ? key_off : 0), qh, ql, s,
+                                          fix, l16, g4);
+            softmax_pv_tile<D, 2>(s, bmax, mxh, mx, c0, m_run, l_run, o, vt_s[BUF] + key_off,
+                                  l16, g4);
         }
         __syncthreads();
     };
@@ -1082,33 +1075,8 @@ attention_fwd_split_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 for (int j = 0; j < 4; ++j) o[db][j] += xfer[(4 * db + j) * 64 + lane] * ac;
             l_run += xfer[(4 * L::kDBlocks + 1) * 64 + lane] * ac;
         }
-        m_run = m_new;
-    }
-
-    if (chunk == 0) {
-        const float inv = 1.0f / sum_lane_groups(l_run);
-        if (row < n_patches) {
-            if constexpr (IO == kIoDense) {
-#pragma unroll
-                for (int db = 0; db < L::kDBlocks; ++db)
-                    *reinterpret_cast<T4 *>(og + row * D + 16 * db + 4 * g4) =
-                        __builtin_convertvector(o[db] * inv, T4);
-            } else {
-                T *orow = og + (size_t)row * io.stride_patch;
-#pragma unroll
-                for (int db = 0; db < L::kDBlocks; ++db) {
-                    const int c = 16 * db + 4 * g4;
-                    const T4 y = __builtin_convertvector(o[db] * inv, T4);
-                    if constexpr (IO == kIoVec4) {
-                        if (c < io.head_dim) *reinterpret_cast<T4 *>(orow + c) = y;
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (c + j < io.head_dim) orow[c + j] = y[j];
-                    }
-                }
-            }
-        }
+        store_rows<D, IO, T>(og, o, l_run, qblk * kSplitBlockM + rgroup * kRowsPerWave,
+                             n_patches, io);
     }
 }
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "attention_fwd.hpp"
 
 namespace vattn {
@@ -37,13 +39,12 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int64_t kCusPerDevice = 256;  // MI355X compute units
-
-// AUTO precision: lo terms for key blocks within 16 log2 units (weight
-// > 2^-16) of the running max, in waves whose running max exceeds 24 log2
-// units in magnitude (f16 logit error ~2^-11 * |logit| > 0.01).
-constexpr float kAutoWindow = 16.0f;
-constexpr float kAutoGate = 24.0f;
+// AUTO policy (vattn::AutoPolicy): split-f16 logits for every 16-key block
+// that holds a logit within 20 log2 units of its query's running max.  A
+// key further below weighs less than 2^-20 of the row maximum; there f16
+// P is a subnormal whose spacing (2^-24) already exceeds what the f16
+// logit error (~2^-11 of the logit) changes.
+constexpr float kAutoWindow = 20.0f;
 
 // Largest per-head element span the kernel addresses with 32-bit byte
 // offsets, with headroom below the out-of-range offset the strided loads
@@ -54,115 +55,147 @@ bool overlaps(uintptr_t a, uintptr_t a_bytes, uintptr_t b, uintptr_t b_bytes) {
     return a < b + b_bytes && b < a + a_bytes;
 }
 
-// Correction policy of the SPLIT kernel (see qk_tile): the lo terms go to
-// key blocks within `window` (log2 units) of the running max, for waves
-// whose running max exceeds `gate` in magnitude.
-struct SplitPolicy {
-    float window;
-    float gate;
-};
-
 // Everything a launch needs besides the tensor pointers.
 struct LaunchArgs {
     int n_heads;
     int n_patches;
-    SplitPolicy pol;
+    vattn::AutoPolicy pol;
     vattn::Io io;
     vattn::Rope rope;
     hipStream_t stream;
 };
 
-template <int D, int WAVES, bool SPLIT, int IO, typename T, bool ROPE>
+template <int D, int WAVES, int PREC, int IO, typename T, bool ROPE>
 hipError_t launch(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     constexpr int kBlockM = vattn::Shape<D, WAVES>::kBlockM;
     int n_patches = a.n_patches;
     int q_blocks = (n_patches + kBlockM - 1) / kBlockM;
     int total_blocks = q_blocks * a.n_heads;
-    float window = a.pol.window, gate = a.pol.gate;
+    vattn::AutoPolicy pol = a.pol;
     vattn::Io io = a.io;
     vattn::Rope rope = a.rope;
-    void *args[] = {(void *)&q,            (void *)&k,         (void *)&v,
-                    (void *)&out,          (void *)&n_patches, (void *)&q_blocks,
-                    (void *)&total_blocks, (void *)&window,    (void *)&gate,
-                    (void *)&io,           (void *)&rope};
+    void *args[] = {(void *)&q,         (void *)&k,        (void *)&v,
+                    (void *)&out,       (void *)&n_patches, (void *)&q_blocks,
+                    (void *)&total_blocks, (void *)&pol,   (void *)&io,
+                    (void *)&rope};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, SPLIT, IO, T, ROPE>),
+        reinterpret_cast<const void *>(&vattn::attention_fwd_kernel<D, WAVES, PREC, IO, T, ROPE>),
         dim3((unsigned)total_blocks), dim3(64 * WAVES), args, 0, a.stream);
 }
 
-template <int D, bool SPLIT, int IO, typename T>
+template <int D, int PREC, int IO, typename T>
 hipError_t launch_split_keys(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
     int n_patches = a.n_patches;
     int q_blocks = (n_patches + vattn::kSplitBlockM - 1) / vattn::kSplitBlockM;
     int total_blocks = q_blocks * a.n_heads;
-    float window = a.pol.window, gate = a.pol.gate;
+    vattn::AutoPolicy pol = a.pol;
     vattn::Io io = a.io;
-    void *args[] = {(void *)&q,            (void *)&k,         (void *)&v,
-                    (void *)&out,          (void *)&n_patches, (void *)&q_blocks,
-                    (void *)&total_blocks, (void *)&window,    (void *)&gate,
-                    (void *)&io};
+    void *args[] = {(void *)&q,         (void *)&k,         (void *)&v,
+                    (void *)&out,       (void *)&n_patches, (void *)&q_blocks,
+                    (void *)&total_blocks, (void *)&pol,    (void *)&io};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&vattn::attention_fwd_split_kernel<D, SPLIT, IO, T>),
+        reinterpret_cast<const void *>(&vattn::attention_fwd_split_kernel<D, PREC, IO, T>),
         dim3((unsigned)total_blocks), dim3(1024), args, 0, a.stream);
 }
 
-// Workgroup size.  16 waves (256 query rows) share each K/V tile among the
-// most queries (least L2 traffic and conversion work per query) and run one
-// per CU: used when there are more than half as many of them as CUs.  Then
-// 8-wave blocks would put two workgroups on some CUs, whose 256 rows match
-// the 16-wave block's, but convert each K/V tile twice (AUTO 5-10% slower
-// at 144-204 blocks).  With at most half as many, 8-wave blocks (128 rows)
-// give each busy CU one workgroup: used while they number at least half the
-// CUs.  Below that, the split-key kernel over 64-row blocks (16 waves, 4 per
-// SIMD) while there is at most one such block per CU.  The grids left over
-// (more 64-row blocks than CUs, hence more than 64 wide blocks) run 8-wave
-// blocks on fewer CUs, which beats 64-row 4-wave blocks at one wave per SIMD
-// (3-6% on 20-40 heads of 600-1000 patches).  The rotary kernels skip the
-// 8-wave (it would spill) and split-key steps: 16 waves from half as many
-// blocks, 4-wave blocks below.
-template <int D, bool SPLIT, int IO, typename T, bool ROPE>
-hipError_t launch_any(const T *q, const T *k, const T *v, T *out, const LaunchArgs &a) {
-    const int64_t wide_blocks =
-        (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::Shape<D, 16>::kBlockM - 1) /
-                              vattn::Shape<D, 16>::kBlockM);
-    if (ROPE ? wide_blocks >= kCusPerDevice / 2 : wide_blocks > kCusPerDevice / 2)
-        return launch<D, 16, SPLIT, IO, T, ROPE>(q, k, v, out, a);
-    if constexpr (!ROPE) {
-        if (2 * wide_blocks >= kCusPerDevice)
-            return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
-        const int64_t small_blocks =
-            (int64_t)a.n_heads * (((int64_t)a.n_patches + vattn::kSplitBlockM - 1) /
-                                  vattn::kSplitBlockM);
-        if (small_blocks <= kCusPerDevice)
-            return launch_split_keys<D, SPLIT, IO, T>(q, k, v, out, a);
-        return launch<D, 8, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+// Compute units of the device that owns `stream` (NULL: the current
+// device), queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+hipError_t device_cu_count(hipStream_t stream, int *cus) {
+    int dev = 0;
+    hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    if (n < 1) n = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return hipSuccess;
+}
+
+}  // namespace
+
+// Workgroup shape (see vattn_launch_shape in vattn.h).  16 waves (256 query
+// rows) share each K/V tile among the most queries (least L2 traffic and
+// conversion work per query) and run one per CU: used when there are more
+// of them than half the CUs.  Then 8-wave blocks would put two workgroups
+// on some CUs, whose 256 rows match the 16-wave block's, but convert each
+// K/V tile twice (AUTO 5-10% slower at 144-204 blocks on 256 CUs).  With
+// at most half as many, 8-wave blocks (128 rows) give each CU one
+// workgroup: used while there are as many of them as CUs.  Below that,
+// the split-key kernel over 64-row blocks (16 waves, 4 per SIMD) while
+// there is at most one such block per CU.  The grids left over (more
+// 64-row blocks than CUs, hence more than a quarter of the CUs in wide
+// blocks) run 8-wave blocks on fewer CUs, which beats 64-row 4-wave blocks
+// at one wave per SIMD (3-6% on 20-40 heads of 600-1000 patches).  The
+// rotary kernels skip the 8-wave (it would spill) and split-key steps: 16
+// waves from half as many blocks as CUs, 4-wave blocks below.
+extern "C" int vattn_launch_shape(int n_heads, int n_patches, int head_dim, int rope,
+                                  int cu_count) {
+    if (n_heads < 1 || n_patches < 1 || head_dim < 1 || head_dim > 64 || cu_count < 1)
+        return -VATTN_ERR_SIZE;
+    const int64_t cus = cu_count;
+    const int64_t wide_blocks = (int64_t)n_heads * (((int64_t)n_patches + 255) / 256);
+    if (rope ? 2 * wide_blocks >= cus : 2 * wide_blocks > cus) return VATTN_SHAPE_16_WAVES;
+    if (rope) return VATTN_SHAPE_4_WAVES;
+    if (2 * wide_blocks >= cus) return VATTN_SHAPE_8_WAVES;
+    const int64_t small_blocks = (int64_t)n_heads * (((int64_t)n_patches + 63) / 64);
+    if (small_blocks <= cus) return VATTN_SHAPE_SPLIT_KEYS;
+    return VATTN_SHAPE_8_WAVES;
+}
+
+namespace {
+
+template <int D, int PREC, int IO, typename T, bool ROPE>
+hipError_t launch_any(const T *q, const T *k, const T *v, T *out, int cus, const LaunchArgs &a) {
+    static_assert(vattn::Shape<D, 16>::kBlockM == 256 && vattn::kSplitBlockM == 64,
+                  "vattn_launch_shape counts 256- and 64-row blocks");
+    const int shape = vattn_launch_shape(a.n_heads, a.n_patches, a.io.head_dim, ROPE, cus);
+    if (shape == VATTN_SHAPE_16_WAVES) return launch<D, 16, PREC, IO, T, ROPE>(q, k, v, out, a);
+    if constexpr (ROPE) {
+        return launch<D, 4, PREC, IO, T, ROPE>(q, k, v, out, a);
     } else {
-        return launch<D, 4, SPLIT, IO, T, ROPE>(q, k, v, out, a);
+        if (shape == VATTN_SHAPE_SPLIT_KEYS)
+            return launch_split_keys<D, PREC, IO, T>(q, k, v, out, a);
+        return launch<D, 8, PREC, IO, T, ROPE>(q, k, v, out, a);
     }
 }
 
 template <int D, int IO, typename T, bool ROPE>
-hipError_t launch_mode(const T *q, const T *k, const T *v, T *out, bool split,
+hipError_t launch_mode(const T *q, const T *k, const T *v, T *out, int precision, int cus,
                        const LaunchArgs &a) {
-    return split ? launch_any<D, true, IO, T, ROPE>(q, k, v, out, a)
-                 : launch_any<D, false, IO, T, ROPE>(q, k, v, out, a);
+    if (precision == VATTN_PRECISION_FAST)
+        return launch_any<D, vattn::kPrecFast, IO, T, ROPE>(q, k, v, out, cus, a);
+    if (precision == VATTN_PRECISION_SPLIT)
+        return launch_any<D, vattn::kPrecSplit, IO, T, ROPE>(q, k, v, out, cus, a);
+    return launch_any<D, vattn::kPrecAuto, IO, T, ROPE>(q, k, v, out, cus, a);
 }
 
 template <int D, typename T, bool ROPE>
-hipError_t launch_io(const T *q, const T *k, const T *v, T *out, bool split, int mode,
-                     const LaunchArgs &a) {
+hipError_t launch_io(const T *q, const T *k, const T *v, T *out, int precision, int mode,
+                     int cus, const LaunchArgs &a) {
     if (mode == vattn::kIoDense)
-        return launch_mode<D, vattn::kIoDense, T, ROPE>(q, k, v, out, split, a);
+        return launch_mode<D, vattn::kIoDense, T, ROPE>(q, k, v, out, precision, cus, a);
     if (mode == vattn::kIoVec4)
-        return launch_mode<D, vattn::kIoVec4, T, ROPE>(q, k, v, out, split, a);
-    return launch_mode<D, vattn::kIoScalar, T, ROPE>(q, k, v, out, split, a);
+        return launch_mode<D, vattn::kIoVec4, T, ROPE>(q, k, v, out, precision, cus, a);
+    return launch_mode<D, vattn::kIoScalar, T, ROPE>(q, k, v, out, precision, cus, a);
 }
 
 template <typename T, bool ROPE>
-hipError_t launch_dim(const T *q, const T *k, const T *v, T *out, bool split, int mode,
-                      int D, const LaunchArgs &a) {
-    return D == 64 ? launch_io<64, T, ROPE>(q, k, v, out, split, mode, a)
-                   : launch_io<32, T, ROPE>(q, k, v, out, split, mode, a);
+hipError_t launch_dim(const T *q, const T *k, const T *v, T *out, int precision, int mode,
+                      int D, int cus, const LaunchArgs &a) {
+    return D == 64 ? launch_io<64, T, ROPE>(q, k, v, out, precision, mode, cus, a)
+                   : launch_io<32, T, ROPE>(q, k, v, out, precision, mode, cus, a);
 }
 
 // Checks and dispatch shared by every attention entry point.  rope_dims = 0
@@ -223,17 +256,15 @@ int forward_impl(const T *q, const T *k, const T *v, T *out, int n_heads, int n_
                          (uintptr_t)(N * (rope_dims / 2) * 8)))
         return VATTN_ERR_ALIAS;
 
-    const bool split = precision != VATTN_PRECISION_FAST;
-    const float inf = __builtin_inff();
-    // SPLIT: every key block, every wave.  AUTO: only near-max blocks of
-    // waves whose logits are large (kAutoWindow / kAutoGate).
-    const SplitPolicy pol = precision == VATTN_PRECISION_SPLIT ? SplitPolicy{inf, -1.0f}
-                                                               : SplitPolicy{kAutoWindow, kAutoGate};
+    const vattn::AutoPolicy pol{kAutoWindow};
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const LaunchArgs a{n_heads, n_patches, pol, vattn::Io{stride_head, (int)stride_patch, head_dim},
-                       vattn::Rope{rope_table, rope_dims / 2},
-                       reinterpret_cast<hipStream_t>(stream)};
-    const hipError_t err = rope ? launch_dim<T, true>(q, k, v, out, split, mode, D, a)
-                                : launch_dim<T, false>(q, k, v, out, split, mode, D, a);
+                       vattn::Rope{rope_table, rope_dims / 2}, hs};
+    int cus = 0;
+    hipError_t err = device_cu_count(hs, &cus);
+    if (err == hipSuccess)
+        err = rope ? launch_dim<T, true>(q, k, v, out, precision, mode, D, cus, a)
+                   : launch_dim<T, false>(q, k, v, out, precision, mode, D, cus, a);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return VATTN_ERR_HIP;

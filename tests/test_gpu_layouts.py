@@ -15,6 +15,8 @@ import torch
 import oracle
 import workloads
 
+from tests import full_size
+
 pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-3
@@ -118,15 +120,12 @@ def test_padded_rows_untouched(vattn, d, pitch):
     assert out.data_ptr() == obuf.data_ptr()
 
 
-def test_patch_major_sharp_workload_sampled_rows(vattn):
-    """Workload 6 (the sharp 128 x 4096 x 64 case stored patch-major) at full
-    size, as the benchmark launches it; the oracle computes sampled rows."""
-    w = workloads.WORKLOADS[6]
+def test_patch_major_sharp_workload_full_tensor(vattn):
+    """Workload 6 (the sharp 128 x 4096 x 64 case stored patch-major) as the
+    benchmark launches it; every output element against the oracle."""
     q, k, v = workloads.make_inputs(6)
-    out = _run_patch_major(vattn, q, k, v, "auto").reshape(-1, w.head_dim)
-    rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=8)
-    _assert_close(out[rows], oracle.attention_rows_f64(q, k, v, rows),
-                  "workload 6 (%d rows)" % rows.size)
+    _assert_close(_run_patch_major(vattn, q, k, v, "auto"), full_size.reference(6),
+                  "workload 6")
 
 
 def test_head_dim_40_workload_full(vattn):
@@ -167,17 +166,23 @@ def test_strided_c_abi_direct(vattn):
 # 8-wave blocks again (the rotary kernels use 4-wave blocks there).  The 16-wave kernel stores tiles two steps ahead and
 # synchronises after every odd step, so it also runs with 1, 2, 3 and 5 key
 # tiles (ragged and exact).
-WORKGROUP_SHAPES = [("split keys", 2, 1000), ("split keys ragged", 3, 333),
-                    ("8 waves below the CU count", 20, 1000), ("8 waves", 32, 1000),
-                    ("16 waves above half the CUs", 40, 1000), ("16 waves", 70, 1000),
-                    ("16 waves one tile", 300, 64), ("16 waves two tiles", 300, 128),
-                    ("16 waves three tiles ragged", 300, 150),
-                    ("16 waves five tiles ragged", 260, 300)]
+WORKGROUP_SHAPES = [("split keys", 2, 1000, 1), ("split keys ragged", 3, 333, 1),
+                    ("8 waves below the CU count", 20, 1000, 8), ("8 waves", 32, 1000, 8),
+                    ("16 waves above half the CUs", 40, 1000, 16), ("16 waves", 70, 1000, 16),
+                    ("16 waves one tile", 300, 64, 16), ("16 waves two tiles", 300, 128, 16),
+                    ("16 waves three tiles ragged", 300, 150, 16),
+                    ("16 waves five tiles ragged", 260, 300, 16)]
 
 
-@pytest.mark.parametrize("label,h,n", WORKGROUP_SHAPES, ids=[s[0] for s in WORKGROUP_SHAPES])
+@pytest.mark.parametrize("label,h,n,shape", WORKGROUP_SHAPES,
+                         ids=[s[0] for s in WORKGROUP_SHAPES])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_every_workgroup_shape(vattn, label, h, n, dtype):
+def test_every_workgroup_shape(vattn, label, h, n, shape, dtype):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    chosen = vattn.launch_shape(h, n, 64, False, cus)
+    print("%s: H=%d N=%d, %d CUs, shape %d" % (label, h, n, cus, chosen), flush=True)
+    if cus == 256:
+        assert chosen == shape
     q, k, v = workloads.make_custom(h, n, 64, "sharp", seed=h + n)
     if dtype == "f16":
         q, k, v = (x.astype(np.float16) for x in (q, k, v))

@@ -16,6 +16,8 @@ import torch
 import oracle
 import workloads
 
+from tests import full_size
+
 pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-3
@@ -102,16 +104,14 @@ def test_rope_workload_10_full(vattn, precision):
 
 
 @pytest.mark.parametrize("precision", ["auto", "split"])
-def test_rope_sharp_workload_11_sampled_rows(vattn, precision):
-    """Workload 11 (sharp 128 x 4096 x 64, rotated) at full size, as the
-    benchmark launches it; the oracle computes sampled rows."""
+def test_rope_sharp_workload_11_full_tensor(vattn, precision):
+    """Workload 11 (sharp 128 x 4096 x 64, rotated) as the benchmark launches
+    it; every output element against the oracle."""
     w = workloads.WORKLOADS[11]
     q, k, v = workloads.make_inputs(11)
     table = vattn.rope_table(w.n_patches, w.rope_dims, w.rope_base)
-    got = _run(vattn, q, k, v, table, precision).reshape(-1, w.head_dim)
-    rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=6)
-    _assert_close(got[rows], _ref(q, k, v, w.rope_dims, rows=rows),
-                  "workload 11 %s (%d rows)" % (precision, rows.size))
+    _assert_close(_run(vattn, q, k, v, table, precision), full_size.reference(11),
+                  "workload 11 %s" % precision)
 
 
 # ---------------------------------------------------------------- shapes
