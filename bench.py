@@ -3,11 +3,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 
 One step is one ``vattn_forward`` over the whole workload (every head, every
-query row) on inputs already resident in HBM; the timed steps run as one
-captured HIP graph (``--no-graph``: plain launches).  Prints one JSON line with the
-attention throughput 4*H*N^2*d / time, the roofline of the kernel against
-the dense f16 matrix-core peak, and the float64 CPU oracle timed on a bounded
-sample of the same workload on the host's cores.
+query row) on inputs already resident in HBM.  The K timed steps run as R
+replays of one captured HIP graph of K/R launches (``--no-graph``: plain
+launches), each replay between two HIP events on the launch stream: the
+value is K steps over the whole timed region, and the per-replay times give
+the median / p10 / p90 per step.  Prints one JSON line with the attention
+throughput 4*H*N^2*d / time, the roofline of the kernel (the dense f16
+matrix-core peak, or HBM bandwidth for workloads below the ridge), and the
+float64 CPU oracle timed on a bounded sample of the same workload on every
+core of the process's affinity mask.
 
 Rotary workloads build their (cos, sin) table once, before timing (it
 depends on the positions only, like a weight); a step is then one
@@ -30,6 +34,44 @@ PEAK_F16_TFLOPS = 2516.6   # MI355X dense f16/bf16 matrix peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ("non_causal_flash_amd/csrc/attention_fwd.hpp",
                   "non_causal_flash_amd/csrc/vattn.hip")
+RIDGE_FLOP_PER_BYTE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~315
+
+
+def replay_plan(steps: int, max_replays: int = 10):
+    """(replays, launches per graph) with replays * launches == steps: the
+    largest number of replays up to max_replays that divides steps."""
+    steps = max(1, int(steps))
+    for r in range(min(max_replays, steps), 0, -1):
+        if steps % r == 0:
+            return r, steps // r
+    return 1, steps
+
+
+def roofline_bound(flops: float, algorithmic_bytes: float) -> str:
+    """"mfma" when the workload's arithmetic intensity lies above the ridge
+    point of the dense f16 peak and HBM bandwidth, "hbm" below it."""
+    return "mfma" if flops / algorithmic_bytes >= RIDGE_FLOP_PER_BYTE else "hbm"
+
+
+def percentile(xs, p: float) -> float:
+    """Linear-interpolation percentile of a non-empty sequence."""
+    ys = sorted(xs)
+    if len(ys) == 1:
+        return float(ys[0])
+    pos = (len(ys) - 1) * p / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(ys) - 1)
+    return float(ys[lo] + (ys[hi] - ys[lo]) * (pos - lo))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_hash() -> str:
@@ -104,20 +146,37 @@ def oracle_path(q, k, v, w, n_threads: int = 0, rows=None):
 
 
 def cpu_baseline(q, k, v, w, target_s: float):
-    """The float64 oracle, untuned, on the first heads of the workload."""
-    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")))
+    """The float64 oracle, untuned, on the first heads of the workload, with
+    one OpenMP thread per core of the process's affinity mask; also the
+    single-thread time of the two small workloads (whole tensors).  Returns
+    the record and the oracle output of the heads it computed."""
+    import workloads
+    cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     oracle_path(q[:1], k[:1], v[:1], w, n_threads=cores)
     t1 = time.perf_counter() - t0
     heads = max(1, min(w.n_heads, int(round(target_s / max(t1, 1e-3)))))
     t0 = time.perf_counter()
-    oracle_path(q[:heads], k[:heads], v[:heads], w, n_threads=cores)
+    ref = oracle_path(q[:heads], k[:heads], v[:heads], w, n_threads=cores)
     dt = time.perf_counter() - t0
     flops = 4.0 * heads * w.n_patches ** 2 * w.head_dim
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "first %d of %d heads of %s, every row (%.1f s, float64, %d threads)"
-                      % (heads, w.n_heads, w.name, dt, cores)}
+    single = {}
+    for wid in (1, 2):
+        sw = workloads.WORKLOADS[wid]
+        sq, sk, sv = workloads.make_inputs(wid)
+        best = None
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle_path(sq, sk, sv, sw, n_threads=1)
+            best = min(best or 1e30, time.perf_counter() - t0)
+        single[sw.name] = {"seconds": round(best, 5),
+                           "gflops": round(sw.flops / best / 1e9, 3)}
+    record = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+              "kind": "oracle", "cpu_model": cpu_model(),
+              "sample": "first %d of %d heads of %s, every row (%.1f s, float64, %d threads)"
+                        % (heads, w.n_heads, w.name, dt, cores),
+              "single_thread_best_of_3": single}
+    return record, heads, ref
 
 
 def main():
@@ -165,34 +224,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # The timed steps are issued as one HIP graph of `steps` kernel launches
-    # (captured once, replayed once), so that launches of 10-30 us are not
-    # paced by the Python call path; --no-graph times plain launches.
+    # The K timed steps are issued as R replays of one HIP graph of K/R
+    # kernel launches (captured once), so that launches of 10-30 us are not
+    # paced by the Python call path; --no-graph times plain launches.  HIP
+    # events between the replays, on the launch stream, give per-replay
+    # times; the timed region is bracketed by synchronisations.
+    replays, per_graph = replay_plan(args.steps)
     graph, launch = None, "eager launches"
     if args.graph:
         try:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                for _ in range(args.steps):
+                for _ in range(per_graph):
                     step()
             graph.replay()  # untimed first replay
             torch.cuda.synchronize()
-            launch = "one HIP graph of %d launches" % args.steps
+            launch = "%d replays of one HIP graph of %d launches" % (replays, per_graph)
         except RuntimeError as e:  # fall back to plain launches, and say so
             graph, launch = None, "eager launches (graph capture failed: %s)" % str(e)[:80]
             torch.cuda.synchronize()
 
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for _ in range(args.steps):
-            step()
-    stop.record(stream)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    events[0].record(stream)
+    for r in range(replays):
+        if graph is not None:
+            graph.replay()
+        else:
+            for _ in range(per_graph):
+                step()
+        events[r + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = events[0].elapsed_time(events[-1]) / args.steps
+    per_step = [events[r].elapsed_time(events[r + 1]) / per_graph for r in range(replays)]
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -202,16 +266,27 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    # spot parity on sampled rows (not timed)
+    # spot parity on sampled rows of every head (not timed)
+    host_out = out.contiguous().cpu().numpy().astype(np.float64)
     rows = workloads.sample_rows(w.n_heads, w.n_patches, per_head=2)
-    got = out.contiguous().cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
+    got = host_out.reshape(-1, w.head_dim)[rows]
     ref = oracle_path(q, k, v, w, rows=rows)
     diff = got - ref
     parity = {"rows": int(rows.size), "max_abs": float(np.max(np.abs(diff))),
               "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
 
     tflops = w.flops / (ms * 1e-3) / 1e12
+    gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
     traffic = read_traffic(w.name)
+    bound = roofline_bound(w.flops, w.algorithmic_bytes)
+    if bound == "mfma":
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_F16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                    "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "mfma_frac": round(tflops / PEAK_F16_TFLOPS, 4)}
     record = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -220,6 +295,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_spread": {"replays": replays, "launches_per_replay": per_graph,
+                               "median": round(percentile(per_step, 50), 5),
+                               "p10": round(percentile(per_step, 10), 5),
+                               "p90": round(percentile(per_step, 90), 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -231,16 +310,18 @@ def main():
                            if w.rope_dims else None,
                    "io": "%s %s resident in HBM" % (w.dtype, "[N][H][d]" if w.layout == "patch" else "[H][N][d]"),
                    "launch": launch},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
-                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": traffic},
-        "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "hbm_gbs_algorithmic": round(gbs, 1),
         "counters": read_counters(w.name, args.precision),
         "parity_sample": parity,
     }
     if args.cpu_seconds > 0:
-        record["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_seconds)
+        record["cpu_baseline"], heads, ref_heads = cpu_baseline(q, k, v, w, args.cpu_seconds)
+        # the baseline's heads, compared in full
+        diff = host_out[:heads] - ref_heads
+        record["parity_heads"] = {"heads": heads, "elements": int(diff.size),
+                                  "max_abs": float(np.max(np.abs(diff))),
+                                  "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref_heads))}
     else:
         record["cpu_baseline"] = None
     print(json.dumps(record), flush=True)

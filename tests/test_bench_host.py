@@ -61,3 +61,30 @@ def test_committed_summaries_carry_their_kernel_hash_and_command(name):
     text = open(os.path.join(ROOT, "profiles", name)).read()
     assert "kernel_source_sha256_16:" in text
     assert "rocprofv3 " in text and "python bench.py" in text
+
+
+def test_replay_plan_times_exactly_the_requested_steps():
+    for steps in (1, 5, 7, 20, 30, 50, 97, 100):
+        r, g = bench.replay_plan(steps)
+        assert r * g == steps and 1 <= r <= 10
+    assert bench.replay_plan(50) == (10, 5)
+    assert bench.replay_plan(7) == (7, 1)
+    assert bench.replay_plan(97) == (1, 97)
+
+
+def test_roofline_bound_follows_the_ridge():
+    import workloads
+    kinds = {w.wid: bench.roofline_bound(w.flops, w.algorithmic_bytes)
+             for w in workloads.WORKLOADS.values()}
+    # 4*H*N^2*d flop over 16*H*N*d bytes = N/4 flop per byte; ridge ~315
+    assert kinds[1] == kinds[2] == kinds[3] == "hbm"
+    assert kinds[4] == kinds[5] == "mfma"
+    assert abs(bench.RIDGE_FLOP_PER_BYTE - 314.575) < 1e-3
+
+
+def test_percentile():
+    xs = [5.0, 1.0, 3.0, 2.0, 4.0]
+    assert bench.percentile(xs, 50) == 3.0
+    assert bench.percentile(xs, 0) == 1.0 and bench.percentile(xs, 100) == 5.0
+    assert abs(bench.percentile(xs, 10) - 1.4) < 1e-12
+    assert bench.percentile([7.0], 90) == 7.0
