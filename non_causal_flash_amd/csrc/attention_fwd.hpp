@@ -640,9 +640,10 @@ __device__ __forceinline__ void exp_pv_live(const float4_t (&s)[KB], const float
 // running max is raised only when the tile's
 // max exceeds it by more than kRescaleSlack: then o and l are scaled by
 // 2^(m_old - m_new), s is rebased and c0 follows.  That branch is
-// wave-uniform; it carries its own copy of the exponentials and the P.V
-// product, so the common path joins the rare one only after values both
-// sides compute afresh (no register copies).
+// wave-uniform and only rescales in place; both paths then share one copy
+// of the exponentials and the P.V product (a copy per path made the
+// register allocator merge two homes of o, l and s with ~20 register moves
+// per tile on the common path).
 // bmax, mxh, mx: qk_tile's maxima (tile_maxima).  RECOMPUTE: take them
 // afresh from s instead of keeping qk_tile's across the corrections (fewer
 // live registers, for kernels that are short of them).
@@ -677,10 +678,8 @@ __device__ __forceinline__ void softmax_pv_tile(float4_t (&s)[KB], float (&bmax)
         for (int ks = 0; ks < KB / 2; ++ks) mxh[ks] -= delta;
         c0 -= delta;
         m_run = m_new;
-        exp_pv_live<D, KB>(s, mxh, l_run, o, vt, l16, g4);
-    } else {
-        exp_pv_live<D, KB>(s, mxh, l_run, o, vt, l16, g4);
     }
+    exp_pv_live<D, KB>(s, mxh, l_run, o, vt, l16, g4);
     __builtin_amdgcn_s_setprio(0);
 }
 
