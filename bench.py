@@ -37,12 +37,17 @@ KERNEL_SOURCES = ("non_causal_flash_amd/csrc/attention_fwd.hpp",
 RIDGE_FLOP_PER_BYTE = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~315
 
 
-def replay_plan(steps: int, max_replays: int = 10):
-    """(replays, launches per graph) with replays * launches == steps: the
-    largest number of replays up to max_replays that divides steps."""
+def replay_plan(steps: int, max_replays: int = 10, min_per_graph: int = 10):
+    """(replays, launches per graph) with replays * launches == steps.
+
+    Each graph holds at least min_per_graph launches where the step count
+    allows it (a graph replay costs tens of microseconds of launch gap, which
+    a graph of two 6-20 us launches would put into every step), and among
+    those plans the one with the most replays up to max_replays (the per-replay
+    times give the spread).  Fewer steps than min_per_graph: one graph of all."""
     steps = max(1, int(steps))
     for r in range(min(max_replays, steps), 0, -1):
-        if steps % r == 0:
+        if steps % r == 0 and steps // r >= min(min_per_graph, steps):
             return r, steps // r
     return 1, steps
 
