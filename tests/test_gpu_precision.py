@@ -17,7 +17,11 @@ Families (q scaled by nothing: the caller's scale is part of the input):
   single channel q[:, 0] = 1, k[:, 0] ~ U(hi/4, hi) nats, other channels
                  noise of 0.01: logits that are the whole of |q||k|;
   spread         q = a/8 (all 64 columns), k = u/8 with u ~ U(1/4, 1):
-                 aligned operands spread over every column.
+                 aligned operands spread over every column;
+  large logits   q[:, 0] = a, k[:, 0] ~ U(-a, a), other channels noise of
+                 0.01: logits up to a^2 = 400 or 1600 nats (about 580 or
+                 2300 log2 units, inside the header's ~4096 limit), so the
+                 running max is raised by hundreds of log2 units at a time.
 """
 from __future__ import annotations
 
@@ -103,6 +107,17 @@ def single_channel(h, n, seed, hi=16.0):
     return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
 
 
+def large_logits(h, n, seed, a=20.0):
+    rng = np.random.default_rng(seed)
+    q = np.zeros((h, n, D))
+    q[:, :, 0] = a
+    q[:, :, 1:] = 0.01 * rng.standard_normal((h, n, D - 1))
+    k = 0.01 * rng.standard_normal((h, n, D))
+    k[:, :, 0] = rng.uniform(-a, a, (h, n))
+    v = rng.uniform(-1.0, 1.0, (h, n, D))
+    return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
+
+
 def spread(h, n, seed, a=9.0):
     rng = np.random.default_rng(seed)
     q = np.full((h, n, D), a / 8.0) * (1.0 + 0.01 * rng.standard_normal((h, n, D)))
@@ -122,6 +137,8 @@ FAMILIES = {
     "single_channel_1.25_5": (lambda h, n, s: single_channel(h, n, s, hi=5.0), False),
     # aligned but the 0.01 jitter decorrelates the roundings: FAST passes
     "spread": (spread, False),
+    "large_logits_400": (large_logits, True),
+    "large_logits_1600": (lambda h, n, s: large_logits(h, n, s, a=40.0), True),
 }
 
 # (heads, patches) that select each workgroup shape on 256 CUs; the shape
