@@ -219,7 +219,11 @@ def main():
     out = torch.empty_like(dq)
     if w.layout == "patch":
         dq, dk, dv, out = (t.transpose(0, 1) for t in (dq, dk, dv, out))
-    stream = torch.cuda.current_stream()
+    # Everything from here on runs on one non-default stream (default
+    # priority), the inputs' host-to-device copies finished first.
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.set_stream(stream)
     table = vattn.rope_table(w.n_patches, w.rope_dims, w.rope_base) if w.rope_dims else None
 
     def step():
@@ -244,7 +248,8 @@ def main():
                     step()
             graph.replay()  # untimed first replay
             torch.cuda.synchronize()
-            launch = "%d replays of one HIP graph of %d launches" % (replays, per_graph)
+            launch = ("%d replays of one HIP graph of %d launches, one non-default stream"
+                      % (replays, per_graph))
         except RuntimeError as e:  # fall back to plain launches, and say so
             graph, launch = None, "eager launches (graph capture failed: %s)" % str(e)[:80]
             torch.cuda.synchronize()
