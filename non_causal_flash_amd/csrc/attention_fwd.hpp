@@ -556,7 +556,12 @@ __device__ __forceinline__ unsigned qk_tile(const _Float16 (*kh)[Lds<D>::kKRow],
 }
 
 // q_lo.k_hi (+ q_hi.k_lo) added to the blocks of `mask` (SPLIT: to every
-// block, unconditionally).
+// block, unconditionally).  AUTO at d = 32 (one k-step per block) reads the
+// k_lo fragments of all KB blocks before the per-block branches, so their
+// LDS latency overlaps instead of being waited out inside each branch; the
+// reads for blocks left uncorrected only cost LDS bandwidth.  (Measured:
+// +2 to +4.5% on flat d = 32 inputs, +1.6% on sharp ones; at d = 64 the
+// eight fragments cost more than they save.)
 template <int D, int PREC, bool KLO, int KB>
 __device__ __forceinline__ void apply_corrections(const _Float16 (*kh)[Lds<D>::kKRow],
                                                   const _Float16 (*kl)[Lds<D>::kKRow],
@@ -564,12 +569,27 @@ __device__ __forceinline__ void apply_corrections(const _Float16 (*kh)[Lds<D>::k
                                                   const half8_t (&ql)[Lds<D>::kKSteps],
                                                   float4_t (&s)[KB], unsigned mask, int l16,
                                                   int g4) {
+    if constexpr (PREC == kPrecAuto && KLO && D == 32) {
+        half8_t al[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        if constexpr (PREC == kPrecSplit)
-            qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
-        else if (mask & (1u << kb))
-            qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
+        for (int kb = 0; kb < KB; ++kb)
+            al[kb] = *reinterpret_cast<const half8_t *>(&kl[16 * kb + l16][8 * g4]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if (mask & (1u << kb)) {
+                const half8_t a = *reinterpret_cast<const half8_t *>(&kh[16 * kb + l16][8 * g4]);
+                s[kb] = mfma16(a, ql[0], s[kb]);
+                s[kb] = mfma16(al[kb], qh[0], s[kb]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if constexpr (PREC == kPrecSplit)
+                qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
+            else if (mask & (1u << kb))
+                qk_correct<D, KLO, KB>(kh, kl, qh, ql, s, kb, l16, g4);
+        }
     }
 }
 
